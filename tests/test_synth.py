@@ -35,4 +35,4 @@ def test_bf16_rounding_is_nearest_even():
     f = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 3.0e-3], np.float32)
     r = synth.round_bf16(f)
     assert r[0] == 1.0 and r[1] == 1.0 and r[2] == 1.0 + 2 ** -6 and r[3] == -2.5
-    assert abs(r[4] - 3.0e-3) <= 2 ** -9 * 3.0e-3
+    assert abs(r[4] - 3.0e-3) <= 2 ** -8 * 3.0e-3

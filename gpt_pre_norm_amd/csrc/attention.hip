@@ -1,0 +1,428 @@
+// Causal multi-head scaled dot-product attention.
+//
+// Query i of a sequence sits at absolute position l_past + i and sees keys
+// 0 .. l_past + i; scores are scaled by 1/sqrt(d_h) and normalised with a
+// softmax ("GPT-2 Block - TorchCode", Reference Solution; "Full Forward Pass",
+// How it works, for the cache offset).
+//
+// Three kernels:
+//  * attn_prefill_bf16: flash-style, 128 queries per workgroup (32 per wave),
+//    64-key K/V tiles staged through LDS (double buffered), online softmax in
+//    fp32 with exp2, MFMA 16x16x32 bf16 for Q K^T and P V.  Key tiles past the
+//    causal frontier are never loaded; tiles entirely above a wave's queries
+//    are skipped by that wave; only diagonal tiles apply the mask.
+//  * attn_rows_f32: one wave per query row with a full (max-subtracted)
+//    softmax, for the fp32 mode.
+//  * attn_decode_bf16: one new query per (sequence, head) streaming the cache;
+//    the keys are split over workgroups, each writes (max, sum, unnormalised
+//    output) and a combine kernel merges the splits.
+#include "kernels.h"
+
+namespace gpt2 {
+
+static constexpr float kLog2e = 1.4426950408889634f;
+
+// ================================================================ prefill (bf16, d_h = 64)
+// Vt tile layout in LDS: row d (64 rows of 64 keys, bf16); the 8-byte group of
+// keys 4*kq .. 4*kq+3 sits at group kq ^ vt_swz(d), which keeps the P*V
+// fragment reads free of bank conflicts.
+GPT2_DEV int vt_swz(int d) { return ((d >> 1) & 7) << 1; }
+
+__global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __restrict__ q,
+                                                                KvView kv, bf16_t* __restrict__ o,
+                                                                int H, int T, int l_past, int nqb) {
+  constexpr int D = 64;
+  __shared__ uint4 ks[2][64 * 8];      // K tile [key][8 chunks], swizzled chunks
+  __shared__ uint32_t vt[2][64 * 32];  // V^T tile [d][32 key pairs]
+
+  const int qb = nqb - 1 - (int)blockIdx.y;  // longest rows first
+  const int bh = blockIdx.x;
+  const int b = bh / H, h = bh - (bh / H) * H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+
+  const int q0 = qb * 128;
+  const int qw0 = q0 + wave * 32;                     // this wave's first query (relative)
+  const int kend = l_past + min(q0 + 128, T);         // keys needed by the workgroup
+  const int nkb = (kend + 63) / 64;
+  const int wave_last = l_past + min(qw0 + 31, T - 1);  // last position this wave needs
+
+  const bf16_t* kbase = (const bf16_t*)kv.base + b * kv.sb + h * kv.sh;
+  const bf16_t* vbase = kbase + kv.skv;
+  const bf16_t* qbase = q + (long long)bh * T * D;
+
+  // Q fragments (MFMA B operand): query qw0 + qt*16 + l16, dims ds*32 + 8g .. +7
+  bf16x8_t qf[2][2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int t = min(qw0 + qt * 16 + l16, T - 1);
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds)
+      qf[qt][ds] = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(qbase + (long long)t * D + ds * 32 + 8 * g));
+  }
+
+  // loader mapping: K rows tid>>3 (+32), chunk tid&7; V key pair tid>>3, dims 8*(tid&7)
+  const int lr = tid >> 3, lc = tid & 7;
+  uint4 rk[2], rv[2];
+  auto gload = [&](int kb) {
+    const int key0 = kb * 64;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int key = min(key0 + lr + 32 * i, kend - 1);
+      rk[i] = *reinterpret_cast<const uint4*>(kbase + (long long)key * D + lc * 8);
+      const int vkey = min(key0 + 2 * lr + i, kend - 1);
+      rv[i] = *reinterpret_cast<const uint4*>(vbase + (long long)vkey * D + lc * 8);
+    }
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = lr + 32 * i;
+      ks[st][r * 8 + (lc ^ ((r >> 1) & 7))] = rk[i];
+    }
+    // transpose the key pair (2*lr, 2*lr+1) x dims 8*lc..8*lc+7 into V^T
+    const uint32_t a[4] = {rv[0].x, rv[0].y, rv[0].z, rv[0].w};
+    const uint32_t c[4] = {rv[1].x, rv[1].y, rv[1].z, rv[1].w};
+    const int kq = lr >> 1;          // key quad
+    const int half = lr & 1;         // which pair inside the quad
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = lc * 8 + e;
+      const uint32_t lo = (e & 1) ? (a[e >> 1] >> 16) : (a[e >> 1] & 0xFFFFu);
+      const uint32_t hi = (e & 1) ? (c[e >> 1] >> 16) : (c[e >> 1] & 0xFFFFu);
+      vt[st][d * 32 + ((kq ^ vt_swz(d)) * 2) + half] = lo | (hi << 16);
+    }
+  };
+
+  f32x4_t oacc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) oacc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrun[2] = {-INFINITY, -INFINITY};
+  float lrun[2] = {0.f, 0.f};
+  const float sc = 0.125f * kLog2e;  // 1/sqrt(64), in the log2 domain
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const bool more = kb + 1 < nkb;
+    if (more) gload(kb + 1);
+    const int st = kb & 1;
+    const int key0 = kb * 64;
+    if (key0 <= wave_last) {
+      // ---- S^T = K Q^T for 64 keys x 32 queries
+      f32x4_t s[4][2];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int r = kt * 16 + l16;
+        bf16x8_t kf[2];
+#pragma unroll
+        for (int ds = 0; ds < 2; ++ds) {
+          const int chunk = ds * 4 + g;
+          kf[ds] = __builtin_bit_cast(bf16x8_t, ks[st][r * 8 + (chunk ^ ((r >> 1) & 7))]);
+        }
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qf[qt][0], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1], qf[qt][1], acc, 0, 0, 0);
+          s[kt][qt] = acc;
+        }
+      }
+      // ---- mask (diagonal tiles only), online softmax
+      const bool need_mask = key0 + 63 > l_past + qw0;
+      bf16x8_t pf[2][2];  // [key half j][qt]
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const int qpos = l_past + qw0 + qt * 16 + l16;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float v = s[kt][qt][r] * sc;
+            if (need_mask && key0 + kt * 16 + 4 * g + r > qpos) v = -INFINITY;
+            s[kt][qt][r] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(mrun[qt], mx);
+        const float alpha = __builtin_amdgcn_exp2f(mrun[qt] - mnew);
+        mrun[qt] = mnew;
+        float ls = 0.f;
+        float p[4][4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            p[kt][r] = __builtin_amdgcn_exp2f(s[kt][qt][r] - mnew);
+            ls += p[kt][r];
+          }
+        lrun[qt] = lrun[qt] * alpha + ls;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) oacc[dt][qt][r] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint4 u = make_uint4(pack_bf2(p[2 * j][0], p[2 * j][1]), pack_bf2(p[2 * j][2], p[2 * j][3]),
+                                     pack_bf2(p[2 * j + 1][0], p[2 * j + 1][1]),
+                                     pack_bf2(p[2 * j + 1][2], p[2 * j + 1][3]));
+          pf[j][qt] = __builtin_bit_cast(bf16x8_t, u);
+        }
+      }
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int d = dt * 16 + l16;
+        const uint32_t* vrow = &vt[st][d * 32];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int kq1 = 8 * j + g, kq2 = 8 * j + 4 + g;
+          const uint2 x1 = *reinterpret_cast<const uint2*>(vrow + (kq1 ^ vt_swz(d)) * 2);
+          const uint2 x2 = *reinterpret_cast<const uint2*>(vrow + (kq2 ^ vt_swz(d)) * 2);
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(x1.x, x1.y, x2.x, x2.y));
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
+            oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[j][qt], oacc[dt][qt], 0, 0, 0);
+        }
+      }
+    }
+    if (more) lstore((kb + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and store O [B, T, H*64]
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float l = lrun[qt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float inv = 1.0f / l;
+    const int t = qw0 + qt * 16 + l16;
+    if (t < T) {
+      bf16_t* orow = o + ((long long)b * T + t) * (H * D) + h * D;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const f32x4_t v = oacc[dt][qt];
+        store4(orow + dt * 16 + 4 * g, make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv));
+      }
+    }
+  }
+}
+
+void launch_attn_prefill_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int T, int l_past,
+                              hipStream_t s) {
+  const int nqb = (T + 127) / 128;
+  dim3 grid(B * H, nqb);
+  attn_prefill_bf16_kernel<<<grid, 256, 0, s>>>(q, kv, o, H, T, l_past, nqb);
+}
+
+// ================================================================ row-wise (fp32)
+// One wave per query row: scores into LDS, row max, exp, sum, then lanes over
+// the head dimension accumulate p_j v_j and divide by the sum.
+__global__ __launch_bounds__(256) void attn_rows_f32_kernel(const float* __restrict__ q, KvView kv,
+                                                            float* __restrict__ o, int B, int H, int T,
+                                                            int dh, int l_past, int maxk) {
+  extern __shared__ float sbuf[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * 4 + wave;
+  const bool active = row < (long long)B * H * T;
+  float* s = sbuf + wave * maxk;
+  int t = 0, b = 0, h = 0, nk = 0;
+  const float *qv = nullptr, *kb = nullptr, *vb = nullptr;
+  float m = -INFINITY, l = 0.f;
+  if (active) {
+    t = (int)(row % T);
+    const int bh = (int)(row / T);
+    b = bh / H;
+    h = bh - b * H;
+    nk = l_past + t + 1;
+    qv = q + row * dh;
+    kb = (const float*)kv.base + b * kv.sb + h * kv.sh;
+    vb = kb + kv.skv;
+    const float scale = 1.0f / sqrtf((float)dh);
+    for (int j = lane; j < nk; j += 64) {
+      const float* kr = kb + (long long)j * dh;
+      float acc = 0.f;
+      for (int c = 0; c < dh; c += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(qv + c);
+        const float4 k4 = *reinterpret_cast<const float4*>(kr + c);
+        acc = fmaf(a.x, k4.x, acc);
+        acc = fmaf(a.y, k4.y, acc);
+        acc = fmaf(a.z, k4.z, acc);
+        acc = fmaf(a.w, k4.w, acc);
+      }
+      const float v = acc * scale;
+      s[j] = v;
+      m = fmaxf(m, v);
+    }
+  }
+  m = wave_max(m);
+  if (active) {
+    for (int j = lane; j < nk; j += 64) {
+      const float p = expf(s[j] - m);
+      s[j] = p;
+      l += p;
+    }
+  }
+  l = wave_sum(l);
+  __syncthreads();
+  if (active) {
+    const float inv = 1.0f / l;
+    float* orow = o + ((long long)b * T + t) * (H * dh) + h * dh;
+    for (int c = lane; c < dh; c += 64) {
+      float acc = 0.f;
+      for (int j = 0; j < nk; ++j) acc = fmaf(s[j], vb[(long long)j * dh + c], acc);
+      orow[c] = acc * inv;
+    }
+  }
+}
+
+void launch_attn_rows_f32(const float* q, KvView kv, float* o, int B, int H, int T, int d_head,
+                          int l_past, hipStream_t s) {
+  const long long rows = (long long)B * H * T;
+  const int maxk = l_past + T;
+  const int blocks = (int)((rows + 3) / 4);
+  attn_rows_f32_kernel<<<blocks, 256, 4 * maxk * sizeof(float), s>>>(q, kv, o, B, H, T, d_head,
+                                                                     l_past, maxk);
+}
+
+// ================================================================ decode (bf16, d_h = 64)
+static constexpr int kDecKeys = 256;  // keys per workgroup (64 per wave)
+static constexpr int kPart = 64 + 2;  // partial record: max, sum, out[64]
+
+size_t decode_part_floats(int B, int H, int n_keys) {
+  const int ns = (n_keys + kDecKeys - 1) / kDecKeys;
+  return (size_t)B * H * ns * kPart;
+}
+
+// Lane layout inside a wave: 8 lanes per key row (8 dims each), 8 rows per
+// pass, 8 passes = 64 keys; all 16 row loads of a lane are issued together.
+__global__ __launch_bounds__(256) void attn_decode_bf16_kernel(const bf16_t* __restrict__ q, KvView kv,
+                                                               float* __restrict__ part, int H,
+                                                               int nk, int ns) {
+  constexpr int D = 64;
+  __shared__ float wmax[4];
+  __shared__ float wsum[4];
+  __shared__ float wout[4][D];
+  const int split = blockIdx.y, bh = blockIdx.x;
+  const int b = bh / H, h = bh - (bh / H) * H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c8 = lane & 7, rg = lane >> 3;
+
+  const bf16_t* kbase = (const bf16_t*)kv.base + b * kv.sb + h * kv.sh;
+  const bf16_t* vbase = kbase + kv.skv;
+  const int key0 = split * kDecKeys + wave * 64;
+
+  const uint4 qu = *reinterpret_cast<const uint4*>(q + (long long)bh * D + c8 * 8);
+  const float qv[8] = {bf_lo(qu.x), bf_hi(qu.x), bf_lo(qu.y), bf_hi(qu.y),
+                       bf_lo(qu.z), bf_hi(qu.z), bf_lo(qu.w), bf_hi(qu.w)};
+  uint4 kr[8], vr[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int key = min(key0 + rg + 8 * i, nk - 1);
+    kr[i] = *reinterpret_cast<const uint4*>(kbase + (long long)key * D + c8 * 8);
+    vr[i] = *reinterpret_cast<const uint4*>(vbase + (long long)key * D + c8 * 8);
+  }
+  const float sc = 0.125f * kLog2e;
+  float sv[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 u = kr[i];
+    float acc = qv[0] * bf_lo(u.x);
+    acc = fmaf(qv[1], bf_hi(u.x), acc);
+    acc = fmaf(qv[2], bf_lo(u.y), acc);
+    acc = fmaf(qv[3], bf_hi(u.y), acc);
+    acc = fmaf(qv[4], bf_lo(u.z), acc);
+    acc = fmaf(qv[5], bf_hi(u.z), acc);
+    acc = fmaf(qv[6], bf_lo(u.w), acc);
+    acc = fmaf(qv[7], bf_hi(u.w), acc);
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    acc += __shfl_xor(acc, 4, 64);
+    const int key = key0 + rg + 8 * i;
+    sv[i] = key < nk ? acc * sc : -INFINITY;
+    mx = fmaxf(mx, sv[i]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 8, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  if (lane == 0) wmax[wave] = mx;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  float l = 0.f;
+  float ov[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = __builtin_amdgcn_exp2f(sv[i] - m);  // 0 for masked keys
+    l += p;
+    const uint4 u = vr[i];
+    ov[0] = fmaf(p, bf_lo(u.x), ov[0]);
+    ov[1] = fmaf(p, bf_hi(u.x), ov[1]);
+    ov[2] = fmaf(p, bf_lo(u.y), ov[2]);
+    ov[3] = fmaf(p, bf_hi(u.y), ov[3]);
+    ov[4] = fmaf(p, bf_lo(u.z), ov[4]);
+    ov[5] = fmaf(p, bf_hi(u.z), ov[5]);
+    ov[6] = fmaf(p, bf_lo(u.w), ov[6]);
+    ov[7] = fmaf(p, bf_hi(u.w), ov[7]);
+  }
+  // sum over the 8 row groups (p is replicated over the 8 lanes of a row)
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1) {
+    l += __shfl_xor(l, off, 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ov[e] += __shfl_xor(ov[e], off, 64);
+  }
+  if (lane < 8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wout[wave][lane * 8 + e] = ov[e];
+  }
+  if (lane == 0) wsum[wave] = l;
+  __syncthreads();
+  if (tid < D + 2) {
+    float* rec = part + ((long long)bh * ns + split) * kPart;
+    if (tid < D)
+      rec[2 + tid] = (wout[0][tid] + wout[1][tid]) + (wout[2][tid] + wout[3][tid]);
+    else if (tid == D)
+      rec[0] = m;
+    else
+      rec[1] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  }
+}
+
+// One wave per (sequence, head); lane = output dim.
+__global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float* __restrict__ part,
+                                                                  bf16_t* __restrict__ o, int BH, int H,
+                                                                  int ns) {
+  constexpr int D = 64;
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= BH) return;
+  const float* rec = part + (long long)bh * ns * kPart;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, rec[s * kPart]);
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = __builtin_amdgcn_exp2f(rec[s * kPart] - M);
+    L = fmaf(rec[s * kPart + 1], w, L);
+    acc = fmaf(rec[s * kPart + 2 + lane], w, acc);
+  }
+  const int b = bh / H, h = bh - (bh / H) * H;
+  o[(long long)b * H * D + h * D + lane] = f2bf(acc / L);
+}
+
+void launch_attn_decode_bf16(const bf16_t* q, KvView kv, bf16_t* o, float* part, int B, int H,
+                             int l_past, hipStream_t s) {
+  const int nk = l_past + 1;
+  const int ns = (nk + kDecKeys - 1) / kDecKeys;
+  attn_decode_bf16_kernel<<<dim3(B * H, ns), 256, 0, s>>>(q, kv, part, H, nk, ns);
+  attn_decode_combine_kernel<<<(B * H + 3) / 4, 256, 0, s>>>(part, o, B * H, H, ns);
+}
+
+}  // namespace gpt2

@@ -1,0 +1,75 @@
+// Shared device helpers for the gfx950 kernels: bf16 conversions, vector
+// types for the MFMA builtins, wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // bfloat16 storage (bit pattern)
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+#define GPT2_DEV __device__ __forceinline__
+
+GPT2_DEV float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+GPT2_DEV bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (bf16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+GPT2_DEV uint32_t pack_bf2(float a, float b) { return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16); }
+
+// Low/high bf16 of a packed pair, as fp32.
+GPT2_DEV float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+GPT2_DEV float bf_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+template <typename T> struct ActT;
+template <> struct ActT<float> {
+  static GPT2_DEV float load(const float* p) { return *p; }
+  static GPT2_DEV void store(float* p, float v) { *p = v; }
+};
+template <> struct ActT<bf16_t> {
+  static GPT2_DEV float load(const bf16_t* p) { return bf2f(*p); }
+  static GPT2_DEV void store(bf16_t* p, float v) { *p = f2bf(v); }
+};
+
+// Four consecutive elements <-> float4 (16 B for fp32, 8 B for bf16).
+GPT2_DEV float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+GPT2_DEV float4 load4(const bf16_t* p) {
+  uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y));
+}
+GPT2_DEV void store4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+GPT2_DEV void store4(bf16_t* p, float4 v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
+}
+
+GPT2_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+GPT2_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+GPT2_DEV float gelu_tanh(float x) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  const float k1 = 0.044715f;
+  return 0.5f * x * (1.0f + tanhf(k0 * (x + k1 * x * x * x)));
+}
+
+// Strided view of a K/V store: element (b, kv, h, pos, j) lives at
+//   base + b*sb + kv*skv + h*sh + pos*d_h + j
+// Covers the cache [B, L, 2, h, cap, d_h] (base offset by the layer) and the
+// block-mode present [B, 2, h, T, d_h].
+struct KvView {
+  void* base;
+  long long sb, skv, sh;
+};

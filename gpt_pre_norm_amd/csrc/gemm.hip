@@ -1,0 +1,324 @@
+// Y = X W^T with fused epilogues, for the five matrix products of the decoder:
+// c_attn (+bias, split into q and the K/V store), attn c_proj and mlp c_proj
+// (+bias +residual), c_fc (+bias, GELU) and the tied head (wte^T, fp32 logits).
+// ("Decoder Block", How it works; "Full Forward Pass", How it works.)
+//
+// bf16 path: MFMA v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Both
+// operands are K-contiguous ([rows, K] row-major), which is the layout the MFMA
+// fragments want.  The W tile is the MFMA A operand and the X tile the B
+// operand, so each lane's four accumulators are four consecutive output
+// columns of one row: the epilogue does 8/16-byte vector stores.
+// Tiles are staged through LDS with a double buffer (one barrier per K step)
+// and an XOR swizzle of the 16-byte chunks so fragment reads are conflict-free.
+//
+// fp32 path: a plain LDS-tiled FMA kernel (correctness mode).
+#include "kernels.h"
+
+namespace gpt2 {
+
+// ================================================================ epilogues
+struct EpiStoreF32 {
+  float* out;
+  int N;
+  GPT2_DEV void operator()(int m, int n, f32x4_t v) const {
+    float* p = out + (long long)m * N + n;
+    if (n + 3 < N) {
+      p[0] = v[0]; p[1] = v[1]; p[2] = v[2]; p[3] = v[3];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) p[r] = v[r];
+    }
+  }
+};
+
+template <typename Tact>
+struct EpiBiasGelu {
+  const Tact* bias;
+  Tact* out;
+  int N;
+  GPT2_DEV void operator()(int m, int n, f32x4_t v) const {
+    const float4 b = load4(bias + n);
+    store4(out + (long long)m * N + n,
+           make_float4(gelu_tanh(v[0] + b.x), gelu_tanh(v[1] + b.y), gelu_tanh(v[2] + b.z),
+                       gelu_tanh(v[3] + b.w)));
+  }
+};
+
+template <typename Tact, typename Tres, typename Tout>
+struct EpiBiasResid {
+  const Tact* bias;
+  const Tres* res;
+  Tout* out;
+  int N;
+  GPT2_DEV void operator()(int m, int n, f32x4_t v) const {
+    const float4 b = load4(bias + n);
+    const long long o = (long long)m * N + n;
+    const float4 r = load4(res + o);
+    store4(out + o, make_float4(r.x + (v[0] + b.x), r.y + (v[1] + b.y), r.z + (v[2] + b.z),
+                                r.w + (v[3] + b.w)));
+  }
+};
+
+template <typename Tact>
+struct EpiQKV {
+  const Tact* bias;
+  Tact* q;
+  KvView kv;
+  int T, l_past, H, dh, d;
+  GPT2_DEV void operator()(int m, int n, f32x4_t v) const {
+    const float4 b = load4(bias + n);
+    const float4 y = make_float4(v[0] + b.x, v[1] + b.y, v[2] + b.z, v[3] + b.w);
+    const int sec = n / d;
+    const int c = n - sec * d;
+    const int h = c / dh;
+    const int j = c - h * dh;
+    const int bi = m / T;
+    const int t = m - bi * T;
+    Tact* dst;
+    if (sec == 0)
+      dst = q + (((long long)bi * H + h) * T + t) * dh + j;
+    else
+      dst = (Tact*)kv.base + bi * kv.sb + (sec - 1) * kv.skv + h * kv.sh +
+            (long long)(l_past + t) * dh + j;
+    store4(dst, y);
+  }
+};
+
+// ================================================================ tile order
+// Maps the hardware block id to an output tile.  Workgroups are dealt to the
+// 8 XCDs round-robin; when the grid divides evenly the ids are regrouped so
+// each XCD walks a contiguous run of logical tiles, then logical tiles are
+// ordered in groups of GM tile-rows so neighbours share X rows and W rows in
+// that XCD's L2.
+GPT2_DEV void tile_coords(int bid, int nb, int tiles_m, int tiles_n, int& tm, int& tn) {
+  int L = bid;
+  if ((nb & 7) == 0) L = (bid & 7) * (nb >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int group = L / per_group;
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int r = L - group * per_group;
+  tm = first_m + r % gsize;
+  tn = r / gsize;
+}
+
+// ================================================================ bf16 MFMA kernel
+template <int BM, int BN, class Epi>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict__ X,
+                                                        const bf16_t* __restrict__ W, int M, int N,
+                                                        int K, Epi epi, int tiles_m, int tiles_n) {
+  constexpr int BK = 64;             // K per stage: 8 chunks of 16 B per row
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int PA = BM / 32, PB = BN / 32;  // 16-byte loads per thread per stage
+  constexpr int STAGE = (BM + BN) * 8;       // uint4 per stage
+  __shared__ uint4 lds[2 * STAGE];
+
+  int tm_idx, tn_idx;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm_idx, tn_idx);
+  const int m0 = tm_idx * BM, n0 = tn_idx * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int lrow = tid >> 3, lchunk = tid & 7;
+
+  const bf16_t* xrow[PA];
+  const bf16_t* wrow[PB];
+#pragma unroll
+  for (int i = 0; i < PA; ++i) xrow[i] = X + (long long)min(m0 + lrow + 32 * i, M - 1) * K;
+#pragma unroll
+  for (int i = 0; i < PB; ++i) wrow[i] = W + (long long)min(n0 + lrow + 32 * i, N - 1) * K;
+
+  uint4 ra[PA], rb[PB];
+  auto gload = [&](int k0) {
+    const int kc = k0 + lchunk * 8;
+    const bool ok = kc < K;
+#pragma unroll
+    for (int i = 0; i < PA; ++i)
+      ra[i] = ok ? *reinterpret_cast<const uint4*>(xrow[i] + kc) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < PB; ++i)
+      rb[i] = ok ? *reinterpret_cast<const uint4*>(wrow[i] + kc) : make_uint4(0, 0, 0, 0);
+  };
+  auto lstore = [&](int stage) {
+    uint4* sa = lds + stage * STAGE;
+    uint4* sb = sa + BM * 8;
+#pragma unroll
+    for (int i = 0; i < PA; ++i) {
+      const int r = lrow + 32 * i;
+      sa[r * 8 + (lchunk ^ ((r >> 1) & 7))] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int r = lrow + 32 * i;
+      sb[r * 8 + (lchunk ^ ((r >> 1) & 7))] = rb[i];
+    }
+  };
+
+  f32x4_t acc[TN][TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (K + BK - 1) / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    if (more) gload((kt + 1) * BK);
+    const uint4* sa = lds + (kt & 1) * STAGE;
+    const uint4* sb = sa + BM * 8;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int chunk = ks * 4 + (lane >> 4);
+      bf16x8_t xa[TM], wb[TN];
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const int r = wm * WM + t * 16 + (lane & 15);
+        uint4 u = sa[r * 8 + (chunk ^ ((r >> 1) & 7))];
+        xa[t] = __builtin_bit_cast(bf16x8_t, u);
+      }
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int r = wn * WN + t * 16 + (lane & 15);
+        uint4 u = sb[r * 8 + (chunk ^ ((r >> 1) & 7))];
+        wb[t] = __builtin_bit_cast(bf16x8_t, u);
+      }
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[a], xa[b], acc[a][b], 0, 0, 0);
+    }
+    if (more) lstore((kt + 1) & 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int a = 0; a < TN; ++a) {
+    const int n = n0 + wn * WN + a * 16 + 4 * (lane >> 4);
+    if (n >= N) continue;
+#pragma unroll
+    for (int b = 0; b < TM; ++b) {
+      const int m = m0 + wm * WM + b * 16 + (lane & 15);
+      if (m < M) epi(m, n, acc[a][b]);
+    }
+  }
+}
+
+template <int BM, int BN, class Epi>
+static void run_bf16(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
+                     hipStream_t s) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  gemm_bf16_kernel<BM, BN, Epi><<<tiles_m * tiles_n, 256, 0, s>>>(X, W, M, N, K, epi, tiles_m, tiles_n);
+}
+
+template <class Epi>
+static void dispatch_bf16(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
+                          hipStream_t s) {
+  if (M <= 64)
+    run_bf16<64, 64>(X, W, M, N, K, epi, s);
+  else
+    run_bf16<128, 128>(X, W, M, N, K, epi, s);
+}
+
+// ================================================================ fp32 FMA kernel
+// 64x64 output tile, K step 16, 256 threads, 4x4 outputs per thread
+// (four consecutive columns per row, as the epilogues expect).
+template <class Epi>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ X,
+                                                       const float* __restrict__ W, int M, int N,
+                                                       int K, Epi epi) {
+  constexpr int BT = 64, BK = 16;
+  __shared__ float xs[BK][BT + 4];
+  __shared__ float ws[BK][BT + 4];
+  const int m0 = blockIdx.y * BT, n0 = blockIdx.x * BT;
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int lr = tid >> 2, lk = (tid & 3) * 4;  // loader: row, k offset
+  const float* xr = X + (long long)min(m0 + lr, M - 1) * K;
+  const float* wr = W + (long long)min(n0 + lr, N - 1) * K;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    const int k = k0 + lk;
+    float4 a = k < K ? *reinterpret_cast<const float4*>(xr + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 b = k < K ? *reinterpret_cast<const float4*>(wr + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    xs[lk + 0][lr] = a.x; xs[lk + 1][lr] = a.y; xs[lk + 2][lr] = a.z; xs[lk + 3][lr] = a.w;
+    ws[lk + 0][lr] = b.x; ws[lk + 1][lr] = b.y; ws[lk + 2][lr] = b.z; ws[lk + 3][lr] = b.w;
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = xs[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = ws[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  const int n = n0 + tx * 4;
+  if (n >= N) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m < M) epi(m, n, f32x4_t{acc[i][0], acc[i][1], acc[i][2], acc[i][3]});
+  }
+}
+
+template <class Epi>
+static void dispatch_f32(const float* X, const float* W, int M, int N, int K, const Epi& epi,
+                         hipStream_t s) {
+  dim3 grid((N + 63) / 64, (M + 63) / 64);
+  gemm_f32_kernel<Epi><<<grid, 256, 0, s>>>(X, W, M, N, K, epi);
+}
+
+// ================================================================ dispatch
+template <typename Tact>
+static void launch_typed(const Tact* X, const Tact* W, int M, int N, int K, const Epilogue& e,
+                         hipStream_t s) {
+  auto go = [&](const auto& epi) {
+    if constexpr (sizeof(Tact) == 2)
+      dispatch_bf16(X, W, M, N, K, epi, s);
+    else
+      dispatch_f32(X, W, M, N, K, epi, s);
+  };
+  switch (e.kind) {
+    case EPI_STORE_F32:
+      go(EpiStoreF32{(float*)e.out, N});
+      break;
+    case EPI_BIAS_GELU:
+      go(EpiBiasGelu<Tact>{(const Tact*)e.bias, (Tact*)e.out, N});
+      break;
+    case EPI_BIAS_RESID:
+      if (e.resid_f32 && e.out_f32)
+        go(EpiBiasResid<Tact, float, float>{(const Tact*)e.bias, (const float*)e.resid, (float*)e.out, N});
+      else if (e.resid_f32)
+        go(EpiBiasResid<Tact, float, Tact>{(const Tact*)e.bias, (const float*)e.resid, (Tact*)e.out, N});
+      else if (e.out_f32)
+        go(EpiBiasResid<Tact, Tact, float>{(const Tact*)e.bias, (const Tact*)e.resid, (float*)e.out, N});
+      else
+        go(EpiBiasResid<Tact, Tact, Tact>{(const Tact*)e.bias, (const Tact*)e.resid, (Tact*)e.out, N});
+      break;
+    case EPI_QKV:
+      go(EpiQKV<Tact>{(const Tact*)e.bias, (Tact*)e.q, e.kv, e.T, e.l_past, e.n_head, e.d_head, e.d});
+      break;
+  }
+}
+
+void launch_gemm(bool bf16, const void* X, const void* W, int M, int N, int K, const Epilogue& e,
+                 hipStream_t s) {
+  if (bf16)
+    launch_typed<bf16_t>((const bf16_t*)X, (const bf16_t*)W, M, N, K, e, s);
+  else
+    launch_typed<float>((const float*)X, (const float*)W, M, N, K, e, s);
+}
+
+}  // namespace gpt2

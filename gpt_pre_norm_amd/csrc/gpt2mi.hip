@@ -1,0 +1,292 @@
+// C ABI of libgpt2mi.so (declared in include/gpt2mi.h): argument checks,
+// workspace carving and the launch sequence of the decoder.
+//
+// Sequence per block ("Decoder Block", How it works; "Full Forward Pass", How
+// it works):
+//   LN1 -> c_attn GEMM (+bias, q and K/V written in place) -> causal attention
+//   -> c_proj GEMM (+bias +residual, fp32 stream) -> LN2 -> c_fc GEMM (+bias,
+//   GELU) -> mlp.c_proj GEMM (+bias +residual).
+// Full forward: embedding -> L blocks -> ln_f -> tied head GEMM (fp32 logits).
+// Decode: the same with T = 1 at position l_past, K/V appended into the cache by
+// the c_attn epilogue and a split-key attention over slots 0 .. l_past.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/gpt2mi.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace gpt2;
+
+constexpr size_t kAlign = 256;
+constexpr size_t kHeader = 256;  // sticky device flags at offset 0
+constexpr long long kMaxTokens = 1LL << 24;
+constexpr int kMaxRowKeysF32 = 8192;  // fp32 row-wise attention keeps a row of scores in LDS
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t x, a, q, o, u, kv, part, total;
+};
+
+// Workspace regions for M = B*T rows: fp32 residual x, LN output a, q, attention
+// output o, MLP hidden u, K/V scratch (when no present/cache is given) and the
+// decode split partials.
+Layout layout(const gpt2_hparams& hp, gpt2_mode mode, int B, int T) {
+  const size_t act = mode == GPT2_BF16 ? 2 : 4;
+  const size_t M = (size_t)B * T, d = (size_t)hp.n_embd;
+  Layout L;
+  size_t off = kHeader;
+  L.x = off;  off += up(M * d * 4);
+  L.a = off;  off += up(M * d * act);
+  L.q = off;  off += up(M * d * act);
+  L.o = off;  off += up(M * d * act);
+  L.u = off;  off += up(M * 4 * d * act);
+  L.kv = off; off += up(2 * M * d * act);
+  L.part = off;
+  off += up(decode_part_floats(B, hp.n_head, hp.n_ctx) * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+gpt2_status check_hparams(const gpt2_hparams* hp, gpt2_mode mode, bool need_model) {
+  if (!hp) return GPT2_E_NULL;
+  if (mode != GPT2_FP32 && mode != GPT2_BF16) return GPT2_E_DTYPE;
+  const int d = hp->n_embd, h = hp->n_head;
+  if (d <= 0 || h <= 0 || d % h != 0 || d > 2048 || d % 8 != 0) return GPT2_E_SHAPE;
+  const int dh = d / h;
+  if (mode == GPT2_BF16 && dh != 64) return GPT2_E_SHAPE;
+  if (mode == GPT2_FP32 && (dh % 4 != 0 || dh > 128)) return GPT2_E_SHAPE;
+  if (hp->n_ctx <= 0) return GPT2_E_SHAPE;
+  if (!(hp->eps >= 0.f) || !std::isfinite(hp->eps)) return GPT2_E_SHAPE;
+  if (need_model && (hp->n_vocab <= 0 || hp->n_layer <= 0)) return GPT2_E_SHAPE;
+  return GPT2_OK;
+}
+
+bool any_null(const gpt2_block_weights& w) {
+  return !w.ln1_g || !w.ln1_b || !w.attn_w || !w.attn_b || !w.proj_w || !w.proj_b || !w.ln2_g ||
+         !w.ln2_b || !w.fc_w || !w.fc_b || !w.fc2_w || !w.fc2_b;
+}
+
+gpt2_status check_weights(const gpt2_hparams& hp, const gpt2_weights* W) {
+  if (!W || !W->wte || !W->wpe || !W->lnf_g || !W->lnf_b || !W->blocks) return GPT2_E_NULL;
+  for (int l = 0; l < hp.n_layer; ++l)
+    if (any_null(W->blocks[l])) return GPT2_E_NULL;
+  return GPT2_OK;
+}
+
+gpt2_status check_common(const gpt2_hparams& hp, gpt2_mode mode, int B, int T, int l_past, void* ws,
+                         size_t ws_bytes) {
+  if (B < 1 || T < 1 || (long long)B * T > kMaxTokens) return GPT2_E_SHAPE;
+  if (l_past < 0 || (long long)l_past + T > hp.n_ctx) return GPT2_E_POSITION;
+  if (mode == GPT2_FP32 && l_past + T > kMaxRowKeysF32) return GPT2_E_SHAPE;
+  if (!ws) return GPT2_E_NULL;
+  if (ws_bytes < layout(hp, mode, B, T).total) return GPT2_E_WORKSPACE;
+  return GPT2_OK;
+}
+
+gpt2_status hip_status() { return hipGetLastError() == hipSuccess ? GPT2_OK : GPT2_E_HIP; }
+
+struct Run {
+  const gpt2_hparams& hp;
+  gpt2_mode mode;
+  int B, T, l_past;
+  bool decode;  // single new token per sequence against the cache
+  char* ws;
+  Layout L;
+  hipStream_t s;
+
+  bool bf16() const { return mode == GPT2_BF16; }
+  size_t act() const { return bf16() ? 2 : 4; }
+  int M() const { return B * T; }
+  void* at(size_t off) const { return ws + off; }
+
+  // One pre-norm block.  x_in: block input (fp32 if x_in_f32, else act dtype);
+  // x1: fp32 stream after the attention residual; y: block output.
+  void block(const gpt2_block_weights& w, const void* x_in, bool x_in_f32, float* x1, void* y,
+             bool y_f32, KvView kv) const {
+    const int d = hp.n_embd, H = hp.n_head, dh = d / H, m = M();
+    const bool b16 = bf16();
+    void* a = at(L.a);
+    void* q = at(L.q);
+    void* o = at(L.o);
+    void* u = at(L.u);
+    // LN1
+    launch_layernorm(x_in_f32 || !b16, b16, x_in, w.ln1_g, w.ln1_b, a, m, d, hp.eps, s);
+    // c_attn: q to [B,H,T,dh], k/v into the view at positions l_past..
+    Epilogue e{};
+    e.kind = EPI_QKV;
+    e.bias = w.attn_b;
+    e.q = q;
+    e.kv = kv;
+    e.T = T;
+    e.l_past = l_past;
+    e.n_head = H;
+    e.d_head = dh;
+    e.d = d;
+    launch_gemm(b16, a, w.attn_w, m, 3 * d, d, e, s);
+    // causal attention -> o [B, T, d]
+    if (!b16)
+      launch_attn_rows_f32((const float*)q, kv, (float*)o, B, H, T, dh, l_past, s);
+    else if (decode)
+      launch_attn_decode_bf16((const bf16_t*)q, kv, (bf16_t*)o, (float*)at(L.part), B, H, l_past, s);
+    else
+      launch_attn_prefill_bf16((const bf16_t*)q, kv, (bf16_t*)o, B, H, T, l_past, s);
+    // c_proj + bias + residual -> x1 (fp32)
+    Epilogue p{};
+    p.kind = EPI_BIAS_RESID;
+    p.bias = w.proj_b;
+    p.resid = x_in;
+    p.resid_f32 = x_in_f32 || !b16;
+    p.out = x1;
+    p.out_f32 = true;
+    launch_gemm(b16, o, w.proj_w, m, d, d, p, s);
+    // LN2, c_fc + GELU
+    launch_layernorm(true, b16, x1, w.ln2_g, w.ln2_b, a, m, d, hp.eps, s);
+    Epilogue f{};
+    f.kind = EPI_BIAS_GELU;
+    f.bias = w.fc_b;
+    f.out = u;
+    launch_gemm(b16, a, w.fc_w, m, 4 * d, d, f, s);
+    // mlp.c_proj + bias + residual -> y
+    Epilogue f2{};
+    f2.kind = EPI_BIAS_RESID;
+    f2.bias = w.fc2_b;
+    f2.resid = x1;
+    f2.resid_f32 = true;
+    f2.out = y;
+    f2.out_f32 = y_f32 || !b16;
+    launch_gemm(b16, u, w.fc2_w, m, d, 4 * d, f2, s);
+  }
+
+  // Cache [B, n_layer, 2, H, cap, dh] viewed at one layer.
+  KvView cache_view(void* data, int cap, int layer) const {
+    const long long H = hp.n_head, dh = hp.n_embd / hp.n_head;
+    const long long per_layer = 2 * H * cap * dh;
+    KvView v;
+    v.base = (char*)data + (size_t)layer * per_layer * act();
+    v.sb = hp.n_layer * per_layer;
+    v.skv = H * cap * dh;
+    v.sh = (long long)cap * dh;
+    return v;
+  }
+  // Present / scratch [B, 2, H, T, dh].
+  KvView present_view(void* data) const {
+    const long long H = hp.n_head, dh = hp.n_embd / hp.n_head;
+    KvView v;
+    v.base = data;
+    v.sb = 2 * H * T * dh;
+    v.skv = H * T * dh;
+    v.sh = (long long)T * dh;
+    return v;
+  }
+
+  // Embedding, L blocks, ln_f, head.
+  void model(const gpt2_weights& W, const int32_t* ids, float* logits, const gpt2_kv* cache) const {
+    const int d = hp.n_embd, m = M();
+    const bool b16 = bf16();
+    float* x = (float*)at(L.x);
+    launch_embed(b16, ids, W.wte, W.wpe, x, m, T, l_past, d, hp.n_vocab, (uint32_t*)ws, s);
+    for (int l = 0; l < hp.n_layer; ++l) {
+      const KvView kv = cache ? cache_view(cache->data, cache->capacity, l) : present_view(at(L.kv));
+      block(W.blocks[l], x, true, x, x, true, kv);
+    }
+    void* a = at(L.a);
+    launch_layernorm(true, b16, x, W.lnf_g, W.lnf_b, a, m, d, hp.eps, s);
+    Epilogue e{};
+    e.kind = EPI_STORE_F32;
+    e.out = logits;
+    launch_gemm(b16, a, W.wte, m, hp.n_vocab, d, e, s);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* gpt2_status_str(gpt2_status st) {
+  switch (st) {
+    case GPT2_OK: return "ok";
+    case GPT2_E_NULL: return "a required pointer is NULL";
+    case GPT2_E_SHAPE: return "unsupported or inconsistent sizes";
+    case GPT2_E_DTYPE: return "unknown mode";
+    case GPT2_E_POSITION: return "positions exceed n_ctx or the cache capacity";
+    case GPT2_E_WORKSPACE: return "workspace too small";
+    case GPT2_E_TOKEN: return "token id outside [0, n_vocab)";
+    case GPT2_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t gpt2_workspace_size(const gpt2_hparams* hp, gpt2_mode mode, int32_t B, int32_t T) {
+  if (check_hparams(hp, mode, false) != GPT2_OK) return 0;
+  if (B < 1 || T < 1 || (long long)B * T > kMaxTokens) return 0;
+  return layout(*hp, mode, B, T).total;
+}
+
+gpt2_status gpt2_block_forward(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_block_weights* w,
+                               const void* x, void* y, int32_t B, int32_t T, void* present, void* ws,
+                               size_t ws_bytes, void* stream) {
+  gpt2_status st = check_hparams(hp, mode, false);
+  if (st != GPT2_OK) return st;
+  if (!w || !x || !y) return GPT2_E_NULL;
+  if (any_null(*w)) return GPT2_E_NULL;
+  st = check_common(*hp, mode, B, T, 0, ws, ws_bytes);
+  if (st != GPT2_OK) return st;
+  (void)hipGetLastError();
+  Run r{*hp, mode, B, T, 0, false, (char*)ws, layout(*hp, mode, B, T), (hipStream_t)stream};
+  const KvView kv = r.present_view(present ? present : r.at(r.L.kv));
+  r.block(*w, x, mode == GPT2_FP32, (float*)r.at(r.L.x), y, mode == GPT2_FP32, kv);
+  return hip_status();
+}
+
+gpt2_status gpt2_forward(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_weights* W,
+                         const int32_t* ids, int32_t B, int32_t T, float* logits,
+                         const gpt2_kv* present, void* ws, size_t ws_bytes, void* stream) {
+  gpt2_status st = check_hparams(hp, mode, true);
+  if (st != GPT2_OK) return st;
+  if (!ids || !logits) return GPT2_E_NULL;
+  if ((st = check_weights(*hp, W)) != GPT2_OK) return st;
+  if (present && !present->data) return GPT2_E_NULL;
+  st = check_common(*hp, mode, B, T, 0, ws, ws_bytes);
+  if (st != GPT2_OK) return st;
+  if (present && present->capacity < T) return GPT2_E_POSITION;
+  (void)hipGetLastError();
+  Run r{*hp, mode, B, T, 0, false, (char*)ws, layout(*hp, mode, B, T), (hipStream_t)stream};
+  r.model(*W, ids, logits, present);
+  return hip_status();
+}
+
+gpt2_status gpt2_decode_step(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_weights* W,
+                             const int32_t* ids, int32_t B, int32_t l_past, const gpt2_kv* cache,
+                             float* logits, void* ws, size_t ws_bytes, void* stream) {
+  gpt2_status st = check_hparams(hp, mode, true);
+  if (st != GPT2_OK) return st;
+  if (!ids || !logits || !cache) return GPT2_E_NULL;
+  if (!cache->data) return GPT2_E_NULL;
+  if ((st = check_weights(*hp, W)) != GPT2_OK) return st;
+  st = check_common(*hp, mode, B, 1, l_past, ws, ws_bytes);
+  if (st != GPT2_OK) return st;
+  if (l_past >= cache->capacity) return GPT2_E_POSITION;
+  (void)hipGetLastError();
+  Run r{*hp, mode, B, 1, l_past, true, (char*)ws, layout(*hp, mode, B, 1), (hipStream_t)stream};
+  r.model(*W, ids, logits, cache);
+  return hip_status();
+}
+
+gpt2_status gpt2_read_device_flags(void* ws, void* stream) {
+  if (!ws) return GPT2_E_NULL;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return GPT2_E_HIP;
+  uint32_t flags = 0;
+  if (hipMemcpy(&flags, ws, sizeof(flags), hipMemcpyDeviceToHost) != hipSuccess) return GPT2_E_HIP;
+  if (flags == 0) return GPT2_OK;
+  if (hipMemset(ws, 0, sizeof(flags)) != hipSuccess) return GPT2_E_HIP;
+  if (hipDeviceSynchronize() != hipSuccess) return GPT2_E_HIP;
+  return GPT2_E_TOKEN;
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Internal launchers (host side) for the gfx950 kernels of libgpt2mi.so.
+// Every launcher enqueues on `s` and returns without synchronising; shapes
+// have been validated by the C-ABI layer before any launcher is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.cuh"
+
+namespace gpt2 {
+
+// ---------------------------------------------------------------- embedding
+// x[m, :] = wte[ids[m], :] + wpe[l_past + m % T, :]  (fp32 out); a bad id
+// zero-fills the row and ORs 1 into *flags.
+void launch_embed(bool bf16, const int32_t* ids, const void* wte, const void* wpe, float* x,
+                  int M, int T, int l_past, int d, int n_vocab, uint32_t* flags, hipStream_t s);
+
+// ---------------------------------------------------------------- LayerNorm
+// y = LN(x) * g + b over rows of width d; one row per wave.
+// x_f32: x is fp32 (else mode dtype); act_bf16: g, b, y are bf16 (else fp32).
+void launch_layernorm(bool x_f32, bool act_bf16, const void* x, const void* g, const void* b,
+                      void* y, int M, int d, float eps, hipStream_t s);
+
+// ---------------------------------------------------------------- GEMM
+enum EpiKind {
+  EPI_STORE_F32 = 0,   // out fp32 [M, N] = acc                    (tied head)
+  EPI_BIAS_GELU = 1,   // out act [M, N] = gelu(acc + bias)        (c_fc)
+  EPI_BIAS_RESID = 2,  // out = resid + acc + bias                 (c_proj, mlp.c_proj)
+  EPI_QKV = 3          // acc + bias split to q [B,h,T,d_h] and the K/V view (c_attn)
+};
+
+struct Epilogue {
+  EpiKind kind;
+  const void* bias;   // [N], act dtype
+  void* out;          // EPI_STORE_F32 / EPI_BIAS_GELU / EPI_BIAS_RESID
+  const void* resid;  // EPI_BIAS_RESID, [M, N]
+  bool resid_f32;     // residual input is fp32 (else act dtype)
+  bool out_f32;       // EPI_BIAS_RESID output is fp32 (else act dtype)
+  // EPI_QKV
+  void* q;            // [B, h, T, d_h]
+  KvView kv;          // K/V destination for positions l_past .. l_past + T - 1
+  int T, l_past, n_head, d_head, d;
+};
+
+// Y = X W^T with the epilogue; X [M, K], W [N, K] row-major.
+// bf16: MFMA path (K % 8 == 0); else fp32 FMA path (K % 4 == 0).
+void launch_gemm(bool bf16, const void* X, const void* W, int M, int N, int K, const Epilogue& e,
+                 hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+// Causal attention for T new queries per sequence at positions l_past .. l_past+T-1
+// against keys 0 .. l_past+T-1 from the K/V view; q [B, h, T, d_h];
+// o [B, T, h*d_h] (act dtype).
+// Prefill (bf16, d_h == 64): flash kernel with MFMA.
+void launch_attn_prefill_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int T, int l_past,
+                              hipStream_t s);
+// Row-wise reference-style kernel (fp32 mode, any T, d_h % 4 == 0, d_h <= 128).
+void launch_attn_rows_f32(const float* q, KvView kv, float* o, int B, int H, int T, int d_head,
+                          int l_past, hipStream_t s);
+// Single-token decode (bf16, d_h == 64): split over keys + combine.
+// part: workspace of decode_part_floats(B, H, l_past) floats.
+size_t decode_part_floats(int B, int H, int n_keys);
+void launch_attn_decode_bf16(const bf16_t* q, KvView kv, bf16_t* o, float* part, int B, int H,
+                             int l_past, hipStream_t s);
+
+}  // namespace gpt2

@@ -1,0 +1,140 @@
+/* gpt2mi.h - C ABI of libgpt2mi.so: the GPT-2 pre-norm decoder forward and its
+ * cached single-token decode step on one AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (web pages, cited by title and section):
+ *   "Decoder Block" (GPT-2, AI Engineer Exhaustive), How it works: one pre-norm
+ *     block, x <- x + Attn(LN1 x); x <- x + MLP(LN2 x), LayerNorm eps 1e-5,
+ *     causal multi-head attention with a fused QKV projection (c_attn) and an
+ *     output projection (c_proj), a 4d-wide GELU MLP (c_fc, c_proj).
+ *   "Full Forward Pass" (GPT-2, AI Engineer Exhaustive), How it works: the
+ *     embedding sum wte[id] + wpe[l_past + t], L blocks, the final ln_f, the tied
+ *     head logits = LN_f(H) wte^T, and the per-layer present (new K, V) stacked
+ *     as [B, L, 2, h, T, d_h]; a cached step feeds only the newest token.
+ *   "GPT-2 Transformer block" (Open Model Atlas), norm() excerpt: mean, biased
+ *     variance of deviations, rsqrt(s + eps), gain, bias.
+ *   "GPT-2 Block - TorchCode", Reference Solution: scores scaled by 1/sqrt(d_h),
+ *     future positions masked.
+ * GELU is the tanh approximation 0.5x(1 + tanh(sqrt(2/pi)(x + 0.044715x^3))).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers must be device memory (hipMalloc or a
+ *     torch CUDA tensor) on the current device; host structs (gpt2_hparams,
+ *     gpt2_weights, gpt2_block_weights, gpt2_kv) are read only during the call.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronises on the compute path; work is enqueued on `stream` (a
+ *     hipStream_t; NULL is the default stream) and runs asynchronously.
+ *   - All tensors are dense row-major.  Linear weights are stored [out, in]
+ *     (y = x W^T + b); wte is [n_vocab, n_embd], wpe is [n_ctx, n_embd].
+ *   - GPT2_BF16: weights, LayerNorm gains/biases, linear biases, block-mode x and y
+ *     and the K/V cache are bfloat16; matrix products accumulate in fp32; the
+ *     residual stream inside gpt2_forward / gpt2_decode_step is fp32; logits are
+ *     fp32.  GPT2_FP32: every tensor is fp32 and all arithmetic is fp32.
+ *   - Argument errors are detected on the host before anything is enqueued and
+ *     are returned as a status; nothing is launched then.  A launch failure is
+ *     GPT2_E_HIP.  An out-of-range token id cannot be seen without a sync: the
+ *     embedding kernel zero-fills that row and raises a sticky device flag in
+ *     the workspace that gpt2_read_device_flags reports and clears.
+ *   - Concurrent calls must use distinct workspaces.
+ */
+#ifndef GPT2MI_H
+#define GPT2MI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPT2_OK = 0,
+  GPT2_E_NULL = 1,      /* a required pointer is NULL */
+  GPT2_E_SHAPE = 2,     /* unsupported or inconsistent sizes */
+  GPT2_E_DTYPE = 3,     /* unknown mode */
+  GPT2_E_POSITION = 4,  /* l_past + T exceeds n_ctx or the cache capacity */
+  GPT2_E_WORKSPACE = 5, /* ws_bytes smaller than gpt2_workspace_size() */
+  GPT2_E_TOKEN = 6,     /* a token id was outside [0, n_vocab) (device flag) */
+  GPT2_E_HIP = 7        /* the HIP runtime reported an error */
+} gpt2_status;
+
+typedef enum { GPT2_FP32 = 0, GPT2_BF16 = 1 } gpt2_mode;
+
+/* Model sizes ("Full Forward Pass", Overview: n_vocab, n_ctx, n_embd, n_head,
+ * n_layer) and the LayerNorm epsilon (1e-5 on the pages).
+ * Supported: n_embd % n_head == 0, n_embd <= 2048, n_embd % 8 == 0;
+ * head width d_h = n_embd / n_head must be 64 in GPT2_BF16 mode and a multiple
+ * of 4 no larger than 128 in GPT2_FP32 mode. */
+typedef struct {
+  int32_t n_vocab, n_ctx, n_embd, n_head, n_layer;
+  float eps;
+} gpt2_hparams;
+
+/* One block's parameters (device pointers, mode dtype; d = n_embd):
+ * ln1_g, ln1_b [d]; attn_w [3d, d], attn_b [3d] (rows: q | k | v, head j owns
+ * rows j*d_h .. of each third); proj_w [d, d], proj_b [d]; ln2_g, ln2_b [d];
+ * fc_w [4d, d], fc_b [4d]; fc2_w [d, 4d], fc2_b [d]. */
+typedef struct {
+  const void *ln1_g, *ln1_b, *attn_w, *attn_b, *proj_w, *proj_b;
+  const void *ln2_g, *ln2_b, *fc_w, *fc_b, *fc2_w, *fc2_b;
+} gpt2_block_weights;
+
+/* Whole-model parameters: wte [n_vocab, d] (also the tied head), wpe [n_ctx, d],
+ * lnf_g, lnf_b [d] (device pointers), blocks: host array of n_layer entries. */
+typedef struct {
+  const void *wte, *wpe, *lnf_g, *lnf_b;
+  const gpt2_block_weights *blocks;
+} gpt2_weights;
+
+/* K/V cache (device memory, mode dtype), layout [B, n_layer, 2, n_head,
+ * capacity, d_h]; index 0 of the third axis is K, 1 is V; slot s holds the
+ * key/value of absolute position s. */
+typedef struct {
+  void *data;
+  int32_t capacity;
+} gpt2_kv;
+
+/* Bytes of workspace any of the three compute calls needs for batch B and
+ * T new tokens per sequence (T = 1 for gpt2_decode_step).  0 on bad arguments.
+ * A new workspace must be zero-filled once before its first use (the first
+ * 256 bytes hold the sticky device flags). */
+size_t gpt2_workspace_size(const gpt2_hparams *hp, gpt2_mode mode, int32_t B, int32_t T);
+
+/* One pre-norm block ("Decoder Block", How it works) on x [B, T, d] -> y [B, T, d]
+ * (device, mode dtype; x and y must not overlap).  Positions are 0..T-1 (no past).
+ * present (device, may be NULL): receives the block's new K, V as
+ * [B, 2, n_head, T, d_h].  Requires 1 <= T <= n_ctx.  n_vocab and n_layer are
+ * not used. */
+gpt2_status gpt2_block_forward(const gpt2_hparams *hp, gpt2_mode mode, const gpt2_block_weights *w,
+                               const void *x, void *y, int32_t B, int32_t T, void *present,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/* Uncached full forward ("Full Forward Pass", How it works): ids [B, T] int32
+ * (device) at positions 0..T-1 -> logits [B, T, n_vocab] fp32 (device).
+ * present (may be NULL): a cache with capacity >= T whose slots 0..T-1 of every
+ * layer receive the new K, V (the stacked present).  Requires 1 <= T <= n_ctx. */
+gpt2_status gpt2_forward(const gpt2_hparams *hp, gpt2_mode mode, const gpt2_weights *W,
+                         const int32_t *ids, int32_t B, int32_t T, float *logits,
+                         const gpt2_kv *present, void *ws, size_t ws_bytes, void *stream);
+
+/* One cached decode step ("Full Forward Pass", How it works, last paragraph):
+ * ids [B] int32 (device) are the newest tokens at position l_past; the cache
+ * holds slots 0..l_past-1 of every layer and receives the new K, V at slot
+ * l_past; each layer attends over slots 0..l_past.  logits [B, 1, n_vocab] fp32.
+ * Requires 0 <= l_past < min(n_ctx, cache->capacity). */
+gpt2_status gpt2_decode_step(const gpt2_hparams *hp, gpt2_mode mode, const gpt2_weights *W,
+                             const int32_t *ids, int32_t B, int32_t l_past, const gpt2_kv *cache,
+                             float *logits, void *ws, size_t ws_bytes, void *stream);
+
+/* Synchronises `stream`, then reads and clears the workspace's sticky device
+ * flags: GPT2_E_TOKEN if any earlier call on this workspace saw a token id
+ * outside [0, n_vocab), else GPT2_OK (or GPT2_E_HIP). */
+gpt2_status gpt2_read_device_flags(void *ws, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *gpt2_status_str(gpt2_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPT2MI_H */

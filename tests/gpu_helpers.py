@@ -1,0 +1,105 @@
+"""Shared helpers for the GPU parity tests: run the HIP path through the C-ABI
+binding, run the oracle on the same seeded inputs, compare."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from gpt_pre_norm_amd import gpt2mi as G
+from gpt_pre_norm_amd import synth
+from oracle import gpt2_oracle as O
+
+# fp32 mode: max relative error max|g - o| / max|o| per output tensor
+TOL_FP32_REL = 1e-4
+# bf16 mode: max absolute error on block outputs and logits
+TOL_BF16_ABS = 3e-2
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+def max_rel(g, o) -> float:
+    g, o = np.asarray(g, np.float64), np.asarray(o, np.float64)
+    return float(np.abs(g - o).max() / np.abs(o).max())
+
+
+def max_abs(g, o) -> float:
+    return float(np.abs(np.asarray(g, np.float64) - np.asarray(o, np.float64)).max())
+
+
+def argmax_agreement(g_logits, o_logits, tol=TOL_BF16_ABS):
+    """(tolerant, raw): a row agrees tolerantly when the oracle's logit at the
+    GPU's argmax is within tol of the oracle's maximum (several tokens are
+    correct within the stated logit tolerance); raw is plain argmax equality."""
+    g = np.asarray(g_logits).reshape(-1, g_logits.shape[-1])
+    o = np.asarray(o_logits, np.float64).reshape(-1, o_logits.shape[-1])
+    ga = g.argmax(-1)
+    tolerant = (o[np.arange(len(ga)), ga] >= o.max(-1) - tol).mean()
+    raw = (ga == o.argmax(-1)).mean()
+    return float(tolerant), float(raw)
+
+
+def check(name, g, o, mode):
+    if mode == G.FP32:
+        err = max_rel(g, o)
+        log(f"  {name}: max rel err {err:.3e} (gate {TOL_FP32_REL})")
+        assert err <= TOL_FP32_REL, (name, err)
+    else:
+        err = max_abs(g, o)
+        log(f"  {name}: max abs err {err:.3e} (gate {TOL_BF16_ABS})")
+        assert err <= TOL_BF16_ABS, (name, err)
+    return err
+
+
+def hp_of(n_vocab, n_ctx, d, h, L):
+    return G.hparams(n_vocab=n_vocab, n_ctx=n_ctx, n_embd=d, n_head=h, n_layer=L, eps=1e-5)
+
+
+def act_dtype(mode):
+    return torch.bfloat16 if mode == G.BF16 else torch.float32
+
+
+# ---------------------------------------------------------------- runners
+
+def run_block(mode, d, h, x, w, present=True, n_ctx=1024):
+    """x: host [B, T, d]; w: host block weights.  Returns (y, present) as numpy."""
+    B, T, _ = x.shape
+    hp = hp_of(1, max(n_ctx, T), d, h, 1)
+    dev_w = G.upload_block(w, mode)
+    xd = G.to_device(x, mode)
+    y = torch.empty_like(xd)
+    pres = torch.empty((B, 2, h, T, d // h), dtype=act_dtype(mode), device="cuda") if present else None
+    ws = G.workspace(hp, mode, B, T)
+    G.block_forward(hp, mode, dev_w, xd, y, B, T, present=pres, ws=ws)
+    torch.cuda.synchronize()
+    return to_np(y), (to_np(pres) if present else None)
+
+
+def run_forward(mode, hp, Wdev, ids, cache=None, capacity=None):
+    B, T = ids.shape
+    idd = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
+    logits = torch.empty((B, T, hp.n_vocab), dtype=torch.float32, device="cuda")
+    ws = G.workspace(hp, mode, B, T)
+    G.forward(hp, mode, Wdev, idd, B, T, logits, present=cache, capacity=capacity, ws=ws)
+    torch.cuda.synchronize()
+    st = G.read_device_flags(ws)
+    return logits, st
+
+
+def run_decode(mode, hp, Wdev, ids, l_past, cache, capacity):
+    B = ids.shape[0]
+    idd = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
+    logits = torch.empty((B, 1, hp.n_vocab), dtype=torch.float32, device="cuda")
+    ws = G.workspace(hp, mode, B, 1)
+    G.decode_step(hp, mode, Wdev, idd, B, l_past, cache, capacity, logits, ws=ws)
+    torch.cuda.synchronize()
+    return logits
+
+
+def new_cache(mode, B, L, h, cap, dh):
+    return torch.zeros((B, L, 2, h, cap, dh), dtype=act_dtype(mode), device="cuda")

@@ -1,0 +1,107 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry point,
+and its host-side argument checks return the documented status codes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gpt_pre_norm_amd import gpt2mi as G
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gpt2mi.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gpt2_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = G.load()
+    names = declared_functions()
+    assert set(names) == set(G.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for st in range(8):
+        assert G.status_str(st)
+    assert G.status_str(6).startswith("token id")
+
+
+def test_workspace_size_host_logic():
+    hp = G.hparams()
+    small = G.workspace_size(hp, G.BF16, 1, 1)
+    big = G.workspace_size(hp, G.BF16, 8, 1024)
+    assert 0 < small < big
+    assert G.workspace_size(hp, G.FP32, 8, 1024) > big
+    assert G.workspace_size(hp, 5, 1, 1) == 0
+    assert G.workspace_size(G.hparams(n_embd=770, n_head=10), G.BF16, 1, 1) == 0  # d_h = 77
+    assert G.workspace_size(G.hparams(n_embd=64, n_head=4), G.BF16, 1, 1) == 0    # bf16 needs d_h 64
+    assert G.workspace_size(G.hparams(n_embd=64, n_head=4), G.FP32, 1, 1) > 0
+    assert G.workspace_size(hp, G.BF16, 0, 1) == 0
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails its host-side checks
+
+
+def _block_weights():
+    return G.BlockWeights(*([FAKE] * 12))
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("bad_mode", 3), ("bad_heads", 2), ("null_x", 1), ("null_weight", 1), ("T_over_ctx", 4),
+    ("zero_B", 2), ("small_ws", 5), ("null_ws", 1)])
+def test_block_forward_argument_errors(case, expect):
+    lib = G.load()
+    hp = G.hparams(n_ctx=16)
+    mode, B, T, x, ws, nbytes = G.BF16, 1, 4, FAKE, FAKE, 1 << 40
+    w = _block_weights()
+    if case == "bad_mode":
+        mode = 7
+    elif case == "bad_heads":
+        hp = G.hparams(n_embd=768, n_head=7)
+    elif case == "null_x":
+        x = None
+    elif case == "null_weight":
+        w.fc_b = None
+    elif case == "T_over_ctx":
+        T = 17
+    elif case == "zero_B":
+        B = 0
+    elif case == "small_ws":
+        nbytes = 1024
+    elif case == "null_ws":
+        ws = None
+    st = lib.gpt2_block_forward(ctypes.byref(hp), mode, ctypes.byref(w), x, FAKE, B, T, None, ws, nbytes,
+                                None)
+    assert st == expect, (st, G.STATUS.get(st))
+
+
+def test_decode_and_forward_position_errors():
+    lib = G.load()
+    hp = G.hparams(n_ctx=1024, n_layer=2)
+    blocks = (G.BlockWeights * 2)(_block_weights(), _block_weights())
+    W = G.Weights(FAKE, FAKE, FAKE, FAKE, ctypes.cast(blocks, ctypes.POINTER(G.BlockWeights)))
+    kv = G.KV(FAKE, 1024)
+    big = 1 << 40
+    # l_past + 1 must stay within n_ctx ("strictly below n_ctx")
+    assert lib.gpt2_decode_step(ctypes.byref(hp), G.BF16, ctypes.byref(W), FAKE, 4, 1024, ctypes.byref(kv),
+                                FAKE, FAKE, big, None) == 4
+    assert lib.gpt2_decode_step(ctypes.byref(hp), G.BF16, ctypes.byref(W), FAKE, 4, -1, ctypes.byref(kv),
+                                FAKE, FAKE, big, None) == 4
+    small = G.KV(FAKE, 100)
+    assert lib.gpt2_decode_step(ctypes.byref(hp), G.BF16, ctypes.byref(W), FAKE, 4, 100, ctypes.byref(small),
+                                FAKE, FAKE, big, None) == 4
+    assert lib.gpt2_forward(ctypes.byref(hp), G.BF16, ctypes.byref(W), FAKE, 2, 1025, FAKE, None, FAKE, big,
+                            None) == 4
+    assert lib.gpt2_forward(ctypes.byref(hp), G.BF16, ctypes.byref(W), FAKE, 2, 200, FAKE, ctypes.byref(small),
+                            FAKE, big, None) == 4
+    assert lib.gpt2_decode_step(ctypes.byref(hp), G.BF16, ctypes.byref(W), FAKE, 4, 5, None, FAKE, FAKE, big,
+                                None) == 1
+    hp0 = G.hparams(n_vocab=0)
+    assert lib.gpt2_forward(ctypes.byref(hp0), G.BF16, ctypes.byref(W), FAKE, 2, 4, FAKE, None, FAKE, big,
+                            None) == 2

@@ -1,0 +1,232 @@
+"""HIP path vs the CPU oracle, element by element, through the C-ABI.
+
+Small cases span several GEMM / attention tiles and a ragged tail; the
+full-size cases run the workloads bench.py times and compare the sequences the
+oracle recomputes (sampled rows for logits).  Gates: fp32 mode max relative
+error <= 1e-4; bf16 mode max absolute error <= 3e-2 and argmax agreement
+(tolerant reading) >= 99.9%.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpt_pre_norm_amd import gpt2mi as G
+from gpt_pre_norm_amd import synth
+from gpt_pre_norm_amd.workloads import WORKLOADS, block_inputs, model_inputs, past_for_sequence
+from gpu_helpers import (TOL_BF16_ABS, argmax_agreement, check, hp_of, log, new_cache, run_block,
+                         run_decode, run_forward, to_np)
+from oracle import gpt2_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    G.load()
+
+
+# ---------------------------------------------------------------- single block
+
+@pytest.mark.parametrize("affine", ["default", "random"])
+def test_block_d64_fp32(affine):
+    wl = WORKLOADS["block_d64_fp32"]
+    x, w = block_inputs(wl, affine)
+    log(f"block fp32 d=64 h=4 x{x.shape} affine={affine}")
+    y, pres = run_block(G.FP32, wl.d, wl.h, x, w)
+    oy, opres = O.block_forward(x, w, wl.h)
+    assert y.shape == (2, 8, 64)
+    check("y", y, oy, G.FP32)
+    check("present", pres, opres, G.FP32)
+
+
+@pytest.mark.parametrize("B,T,d,h", [(3, 77, 96, 3), (1, 130, 128, 2), (2, 1, 32, 8)])
+def test_block_fp32_ragged(B, T, d, h):
+    x = synth.hidden_input((B, T, d), 100 + T)
+    w = synth.block_weights(d, 100 + T, affine="random")
+    log(f"block fp32 B={B} T={T} d={d} h={h}")
+    y, pres = run_block(G.FP32, d, h, x, w)
+    oy, opres = O.block_forward(x, w, h)
+    check("y", y, oy, G.FP32)
+    check("present", pres, opres, G.FP32)
+
+
+@pytest.mark.parametrize("B,T,d", [(2, 200, 768), (3, 129, 128), (1, 1, 64), (2, 64, 192)])
+def test_block_bf16_ragged(B, T, d):
+    h = d // 64
+    x = synth.hidden_input((B, T, d), 200 + T, bf16=True)
+    w = synth.block_weights(d, 200 + T, affine="random", bf16=True)
+    log(f"block bf16 B={B} T={T} d={d} h={h}")
+    y, pres = run_block(G.BF16, d, h, x, w)
+    oy, opres = O.block_forward(x, w, h)
+    check("y", y, oy, G.BF16)
+    check("present", pres, opres, G.BF16)
+
+
+def test_block_gpt2s_bf16_full():
+    """The single-block workload at full size (B=8, T=1024); sequences 0 and 7 vs the oracle."""
+    wl = WORKLOADS["block_gpt2s_bf16"]
+    x, w = block_inputs(wl)
+    log(f"block bf16 full {x.shape}")
+    y, pres = run_block(G.BF16, wl.d, wl.h, x, w)
+    for b in (0, 7):
+        oy, opres = O.block_forward(x[b:b + 1], w, wl.h)
+        check(f"y[{b}]", y[b:b + 1], oy, G.BF16)
+        check(f"present[{b}]", pres[b:b + 1], opres, G.BF16)
+
+
+@pytest.mark.parametrize("mode", [G.FP32, G.BF16])
+def test_block_causality_bit_identical(mode):
+    B, T, d = 2, 150, 128
+    h = 2
+    bf = mode == G.BF16
+    x = synth.hidden_input((B, T, d), 300, bf16=bf)
+    w = synth.block_weights(d, 300, affine="random", bf16=bf)
+    x2 = x.copy()
+    t = 70
+    x2[:, t + 1:] = synth.hidden_input((B, T - t - 1, d), 301, bf16=bf)
+    y1, p1 = run_block(mode, d, h, x, w)
+    y2, p2 = run_block(mode, d, h, x2, w)
+    assert np.array_equal(y1[:, :t + 1], y2[:, :t + 1])
+    assert np.array_equal(p1[..., :t + 1, :], p2[..., :t + 1, :])
+    assert not np.array_equal(y1[:, t + 1:], y2[:, t + 1:])
+
+
+# ---------------------------------------------------------------- full forward
+
+def _small_model(mode, V, n_ctx, d, h, L, seed):
+    bf = mode == G.BF16
+    W = synth.model_weights(V, n_ctx, d, L, seed, affine="random", bf16=bf)
+    return W, G.upload_model(W, mode), hp_of(V, n_ctx, d, h, L)
+
+
+@pytest.mark.parametrize("mode,V,n_ctx,d,h,L,B,T", [
+    (G.FP32, 1001, 64, 64, 4, 2, 2, 37),
+    (G.BF16, 1001, 256, 128, 2, 2, 2, 150),
+    (G.BF16, 517, 64, 64, 1, 3, 3, 1),
+])
+def test_forward_small(mode, V, n_ctx, d, h, L, B, T):
+    W, Wd, hp = _small_model(mode, V, n_ctx, d, h, L, 400 + T)
+    ids = synth.ids_input((B, T), V, 401 + T)
+    cache = new_cache(mode, B, L, h, T + 3, d // h)
+    log(f"forward mode={mode} V={V} d={d} h={h} L={L} B={B} T={T}")
+    logits, st = run_forward(mode, hp, Wd, ids, cache=cache, capacity=T + 3)
+    assert st == 0
+    ol, opres = O.model_forward(ids, W, h)
+    check("logits", to_np(logits), ol, mode)
+    check("present", to_np(cache)[..., :T, :], opres, mode)
+    if mode == G.BF16:
+        tol, raw = argmax_agreement(to_np(logits), ol)
+        log(f"  argmax agreement tolerant {tol:.4f} raw {raw:.4f}")
+        assert tol >= 0.999
+
+
+def test_forward_gpt2s_full():
+    """GPT-2 small forward at full size (B=8, T=1024, V=50257); sequences 0 and 5
+    recomputed by the oracle, 96 sampled logit rows each."""
+    wl = WORKLOADS["gpt2s_fwd_b8_t1024"]
+    ids, W = model_inputs(wl)
+    Wd = G.upload_model(W, wl.mode)
+    hp = hp_of(wl.n_vocab, wl.n_ctx, wl.d, wl.h, wl.L)
+    cache = new_cache(wl.mode, wl.B, wl.L, wl.h, wl.n_ctx, wl.dh)
+    log("forward gpt2-small full size")
+    logits, st = run_forward(wl.mode, hp, Wd, ids, cache=cache, capacity=wl.n_ctx)
+    assert st == 0
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, 511, 1022, 1023], rng.integers(0, 1024, 91)]))
+    g_all = []
+    o_all = []
+    for b in (0, 5):
+        ol, opres = O.model_forward(ids[b:b + 1], W, wl.h, logit_rows=rows)
+        g = to_np(logits[b, torch.from_numpy(rows).cuda()])
+        check(f"logits[{b}] ({len(rows)} rows)", g, ol, wl.mode)
+        check(f"present[{b}]", to_np(cache[b:b + 1]), opres, wl.mode)
+        g_all.append(g)
+        o_all.append(ol)
+    tol, raw = argmax_agreement(np.concatenate(g_all), np.concatenate(o_all))
+    log(f"  argmax agreement tolerant {tol:.4f} raw {raw:.4f}")
+    assert tol >= 0.999
+
+
+@pytest.mark.parametrize("mode", [G.FP32, G.BF16])
+def test_forward_causality_bit_identical(mode):
+    V, n_ctx, d, h, L, B, T = 300, 256, 128, 2, 2, 2, 200
+    W, Wd, hp = _small_model(mode, V, n_ctx, d, h, L, 500)
+    ids = synth.ids_input((B, T), V, 501)
+    ids2 = ids.copy()
+    t = 133
+    ids2[:, t + 1:] = (ids2[:, t + 1:] + 7) % V
+    a, _ = run_forward(mode, hp, Wd, ids)
+    b, _ = run_forward(mode, hp, Wd, ids2)
+    a, b = to_np(a), to_np(b)
+    assert np.array_equal(a[:, :t + 1], b[:, :t + 1])
+    assert not np.array_equal(a[:, t + 1:], b[:, t + 1:])
+
+
+def test_bad_token_sets_flag():
+    V = 100
+    W, Wd, hp = _small_model(G.BF16, V, 64, 64, 1, 1, 600)
+    ids = synth.ids_input((2, 5), V, 601)
+    ids[1, 3] = V
+    _, st = run_forward(G.BF16, hp, Wd, ids)
+    assert st == 6  # GPT2_E_TOKEN
+    ids[1, 3] = 0
+    _, st = run_forward(G.BF16, hp, Wd, ids)
+    assert st == 0
+
+
+# ---------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("mode,V,n_ctx,d,h,L,B,T", [
+    (G.FP32, 211, 64, 64, 4, 2, 3, 20),
+    (G.BF16, 211, 512, 128, 2, 2, 4, 300),
+    (G.BF16, 97, 64, 64, 1, 2, 2, 1),
+])
+def test_decode_matches_uncached(mode, V, n_ctx, d, h, L, B, T):
+    """Forward over T-1 tokens into the cache, then one decode step of token T-1,
+    equals the oracle's uncached pass over T tokens at position T-1."""
+    W, Wd, hp = _small_model(mode, V, n_ctx, d, h, L, 700 + T)
+    ids = synth.ids_input((B, T), V, 701 + T)
+    cap = n_ctx
+    cache = new_cache(mode, B, L, h, cap, d // h)
+    if T > 1:
+        _, st = run_forward(mode, hp, Wd, ids[:, :T - 1], cache=cache, capacity=cap)
+        assert st == 0
+    log(f"decode mode={mode} d={d} L={L} B={B} l_past={T - 1}")
+    step = run_decode(mode, hp, Wd, ids[:, T - 1], T - 1, cache, cap)
+    full, opres = O.model_forward(ids, W, h)
+    check("logits", to_np(step)[:, 0], full[:, T - 1], mode)
+    check("cache slot l_past", to_np(cache)[..., T - 1, :], opres[..., T - 1, :], mode)
+    check("cache slots < l_past", to_np(cache)[..., :T, :], opres, mode)
+
+
+def test_decode_gpt2s_full():
+    """The decode workload at full size: 64 sequences at position 1023 with a
+    random past; sequences 0, 31 and 63 recomputed by the oracle."""
+    wl = WORKLOADS["gpt2s_decode_b64_p1023"]
+    ids, W = model_inputs(wl)
+    ids = ids[:, 0]
+    Wd = G.upload_model(W, wl.mode)
+    hp = hp_of(wl.n_vocab, wl.n_ctx, wl.d, wl.h, wl.L)
+    cap = wl.n_ctx
+    log("decode gpt2-small full size: generating the past")
+    cache = new_cache(wl.mode, wl.B, wl.L, wl.h, cap, wl.dh)
+    per_seq = wl.L * 2 * wl.h * wl.l_past * wl.dh
+    bits = synth.past_bf16_bits((wl.B * per_seq,), wl.seed)
+    past = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    cache[..., :wl.l_past, :] = past.view(wl.B, wl.L, 2, wl.h, wl.l_past, wl.dh)
+    del past, bits
+    step = run_decode(wl.mode, hp, Wd, ids, wl.l_past, cache, cap)
+    g_all, o_all = [], []
+    for b in (0, 31, 63):
+        pb = past_for_sequence(wl, b)[None]
+        ol, opres = O.decode_step(ids[b:b + 1], W, wl.h, past=pb)
+        g = to_np(step[b:b + 1])
+        check(f"logits[{b}]", g, ol, wl.mode)
+        check(f"new K/V[{b}]", to_np(cache[b:b + 1, ..., wl.l_past:wl.l_past + 1, :]), opres, wl.mode)
+        g_all.append(g[:, 0])
+        o_all.append(ol[:, 0])
+    tol, raw = argmax_agreement(np.concatenate(g_all), np.concatenate(o_all))
+    log(f"  argmax agreement tolerant {tol:.4f} raw {raw:.4f}")
+    assert tol >= 0.999

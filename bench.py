@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Throughput of the GPT-2 pre-norm decoder on one MI355X, through the C ABI.
+
+One step = one uncached bf16 forward of GPT-2 small over B=8 sequences of
+T=1024 synthetic tokens (embedding, 12 pre-norm blocks, ln_f, tied head with
+fp32 logits [8, 1024, 50257]).  `value` is tokens/s of that forward.  The same
+run also times the cached decode step (64 sequences, one new token each at
+position 1023 against a random past) and reports it under "decode".
+
+Per-kernel durations come from HIP events the library records around each
+launch (gpt2_timing_begin/end) on the launch stream, in a pass after the
+timed region; the roofline object prices the dominant kernel's algorithmic
+work against MI355X's published peaks.  The CPU oracle is timed on a bounded
+sample of the same workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps K2]
+                       [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s & %bf16 MFMA peak, GPT-2-small fwd B8 T1024; decode tok/s, %HBM"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    return ap.parse_args()
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE counters,
+    committed in profiles/traffic.json together with a hash of the kernel sources;
+    None when absent or when the sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != sources_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def sources_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gpt_pre_norm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(batch sharding is described in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from gpt_pre_norm_amd import gpt2mi as G
+    from gpt_pre_norm_amd import roofline as R
+    from gpt_pre_norm_amd import synth
+    from gpt_pre_norm_amd.workloads import WORKLOADS, model_inputs
+
+    G.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------ forward workload
+    wl = WORKLOADS["gpt2s_fwd_b8_t1024"]
+    log(f"[bench] generating {wl.name}")
+    ids_np, W = model_inputs(wl)
+    Wd = G.upload_model(W, G.BF16)
+    hp = G.hparams(n_vocab=wl.n_vocab, n_ctx=wl.n_ctx, n_embd=wl.d, n_head=wl.h, n_layer=wl.L)
+    ids = torch.from_numpy(ids_np).to(dev)
+    logits = torch.empty((wl.B, wl.T, wl.n_vocab), dtype=torch.float32, device=dev)
+    ws = G.workspace(hp, G.BF16, wl.B, wl.T)
+
+    def fwd():
+        G.forward(hp, G.BF16, Wd, ids, wl.B, wl.T, logits, ws=ws, stream=stream)
+
+    log(f"[bench] forward warmup {args.warmup}")
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    if G.read_device_flags(ws) != 0:
+        raise SystemExit("token flag raised")
+    log(f"[bench] forward timed steps {args.steps}")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        fwd()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = max(wall * 1e3, gpu_ms) / args.steps
+    tokens_per_s = wl.tokens / (ms_per_step / 1e3)
+    flops = R.model_flops(wl.B, wl.T, wl.d, wl.h, wl.L, wl.n_vocab)
+    log(f"[bench] forward {ms_per_step:.3f} ms/step, {tokens_per_s:.4g} tok/s, "
+        f"{flops / (ms_per_step / 1e3) / 1e12:.1f} TFLOP/s")
+
+    # per-kernel pass (events around each launch)
+    G.timing_begin()
+    for _ in range(args.steps):
+        fwd()
+    kt = G.timing_end()
+    work = dict(B=wl.B, T=wl.T, d=wl.d, h=wl.h, V=wl.n_vocab)
+    kernels = {}
+    for name, (n, tot) in sorted(kt.items(), key=lambda kv: -kv[1][1]):
+        f, b = R.kernel_work(name, **work)
+        avg_s = tot / n / 1e3
+        kernels[name] = {"launches_per_step": n / args.steps, "avg_us": round(avg_s * 1e6, 2),
+                         "share": round(tot / sum(v[1] for v in kt.values()), 4),
+                         "tflops": round(f / avg_s / 1e12, 1), "gbps": round(b / avg_s / 1e9, 1)}
+        log(f"[bench]   {name:22s} {n // args.steps:4d}/step avg {avg_s * 1e6:9.2f} us "
+            f"{f / avg_s / 1e12:8.1f} TFLOP/s {b / avg_s / 1e9:8.1f} GB/s")
+    dom = max(kt.items(), key=lambda kv: kv[1][1])[0]
+    f, b = R.kernel_work(dom, **work)
+    n, tot = kt[dom]
+    avg_s = tot / n / 1e3
+    bound = R.bound_of(f, b)
+    if bound == "mfma":
+        achieved, peak, unit = f / avg_s / 1e12, R.PEAK_BF16_FLOPS / 1e12, "TFLOP/s"
+    else:
+        achieved, peak, unit = b / avg_s / 1e9, R.PEAK_HBM_BYTES / 1e9, "GB/s"
+    roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic_for(dom),
+                "work_per_launch": f if bound == "mfma" else b, "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    result = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "GPT-2 small uncached forward, bf16 (fp32 accumulate, fp32 residual "
+                               "stream, fp32 logits), B=8 T=1024, V=50257 d=768 h=12 L=12",
+                   "batch": wl.B, "seq_len": wl.T, "parallelism": "none (1 GPU)"},
+        "tflops": round(flops / (ms_per_step / 1e3) / 1e12, 1),
+        "mfma_peak_frac": round(flops / (ms_per_step / 1e3) / R.PEAK_BF16_FLOPS, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    del logits, ws
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ decode workload
+    if not args.no_decode:
+        result["decode"] = bench_decode(args, G, R, synth, WORKLOADS["gpt2s_decode_b64_p1023"], Wd, hp,
+                                        stream, dev)
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, ids_np, W)
+
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode(args, G, R, synth, wl, Wd, hp, stream, dev):
+    import numpy as np
+    import torch
+
+    log(f"[bench] generating {wl.name} past ({wl.B}x{wl.L}x2x{wl.h}x{wl.l_past}x{wl.dh} bf16)")
+    cap = wl.n_ctx
+    cache = torch.empty((wl.B, wl.L, 2, wl.h, cap, wl.dh), dtype=torch.bfloat16, device=dev)
+    per_seq = wl.L * 2 * wl.h * wl.l_past * wl.dh
+    chunk = 8
+    for b0 in range(0, wl.B, chunk):
+        bits = synth.past_bf16_bits((chunk * per_seq,), wl.seed, start=b0 * per_seq)
+        part = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        cache[b0:b0 + chunk, ..., :wl.l_past, :] = part.view(chunk, wl.L, 2, wl.h, wl.l_past, wl.dh)
+    del part
+    ids = torch.from_numpy(synth.ids_input((wl.B, 1), wl.n_vocab, wl.seed)[:, 0].copy()).to(dev)
+    logits = torch.empty((wl.B, 1, wl.n_vocab), dtype=torch.float32, device=dev)
+    ws = G.workspace(hp, G.BF16, wl.B, 1)
+
+    def step():
+        # rewrites slot l_past with the same K/V each time: steps are idempotent
+        G.decode_step(hp, G.BF16, Wd, ids, wl.B, wl.l_past, cache, cap, logits, ws=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.decode_steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = max(wall * 1e3, ev0.elapsed_time(ev1)) / args.decode_steps
+    byt = R.decode_bytes(wl.B, wl.d, wl.h, wl.L, wl.n_vocab, wl.l_past)
+    log(f"[bench] decode {ms * 1e3:.1f} us/step, {wl.B / (ms / 1e3):.4g} tok/s, "
+        f"{byt / (ms / 1e3) / 1e9:.0f} GB/s algorithmic")
+    G.timing_begin()
+    for _ in range(args.decode_steps):
+        step()
+    kt = G.timing_end()
+    work = dict(B=wl.B, T=1, d=wl.d, h=wl.h, V=wl.n_vocab, l_past=wl.l_past)
+    kernels = {}
+    for name, (n, tot) in sorted(kt.items(), key=lambda kv: -kv[1][1]):
+        f, b = R.kernel_work(name, **work)
+        avg_s = tot / n / 1e3
+        kernels[name] = {"launches_per_step": n / args.decode_steps, "avg_us": round(avg_s * 1e6, 2),
+                         "share": round(tot / sum(v[1] for v in kt.values()), 4),
+                         "gbps": round(b / avg_s / 1e9, 1)}
+        log(f"[bench]   {name:22s} {n // args.decode_steps:4d}/step avg {avg_s * 1e6:9.2f} us "
+            f"{b / avg_s / 1e9:8.1f} GB/s")
+    dom = max(kt.items(), key=lambda kv: kv[1][1])[0]
+    f, b = R.kernel_work(dom, **work)
+    n, tot = kt[dom]
+    avg_s = tot / n / 1e3
+    ach = b / avg_s / 1e9
+    return {
+        "value": round(wl.B / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+        "steps": args.decode_steps,
+        "workload": "GPT-2 small cached decode, bf16, B=64, one new token at position 1023, "
+                    "past [64,12,2,12,1023,64] ~ N(0,1)",
+        "hbm_frac_whole_step": round(byt / (ms / 1e3) / R.PEAK_HBM_BYTES, 4),
+        "algorithmic_bytes_per_step": byt,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": R.PEAK_HBM_BYTES / 1e9,
+                     "unit": "GB/s", "frac": round(ach * 1e9 / R.PEAK_HBM_BYTES, 4),
+                     "traffic": traffic_for(dom), "work_per_launch": b, "avg_launch_us": round(avg_s * 1e6, 2)},
+        "kernels": kernels,
+    }
+
+
+def cpu_baseline(wl, ids_np, W):
+    """The oracle, as it stands, on whole sequences of the forward workload,
+    adding sequences until about 10 s of host time has passed."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import gpt2_oracle as O
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    log(f"[bench] cpu oracle baseline ({threads} BLAS threads)")
+    n = 0
+    t0 = time.perf_counter()
+    while n < wl.B:
+        O.model_forward(ids_np[n:n + 1], W, wl.h)
+        n += 1
+        if time.perf_counter() - t0 > 10.0:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(n * wl.T / el, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {wl.B} sequences (T={wl.T}, full logits), fp64 numpy oracle, {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

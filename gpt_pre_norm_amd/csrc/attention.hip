@@ -8,7 +8,7 @@
 // Three kernels:
 //  * attn_prefill_bf16: flash-style, 128 queries per workgroup (32 per wave),
 //    64-key K/V tiles staged through LDS (double buffered), online softmax in
-//    fp32 with exp2, MFMA 16x16x32 bf16 for Q K^T and P V.  Key tiles past the
+//    fp32 with exp2, MFMA 32x32x16 bf16 for Q K^T and P V.  Key tiles past the
 //    causal frontier are never loaded; tiles entirely above a wave's queries
 //    are skipped by that wave; only diagonal tiles apply the mask.
 //  * attn_rows_f32: one wave per query row with a full (max-subtracted)
@@ -23,43 +23,51 @@ namespace gpt2 {
 static constexpr float kLog2e = 1.4426950408889634f;
 
 // ================================================================ prefill (bf16, d_h = 64)
-// Vt tile layout in LDS: row d (64 rows of 64 keys, bf16); the 8-byte group of
-// keys 4*kq .. 4*kq+3 sits at group kq ^ vt_swz(d), which keeps the P*V
-// fragment reads free of bank conflicts.
-GPT2_DEV int vt_swz(int d) { return ((d >> 1) & 7) << 1; }
+// MFMA v_mfma_f32_32x32x16_bf16 throughout.  A wave owns 32 queries; per 64-key
+// tile it computes S^T = K Q^T (keys on the MFMA rows, queries on the columns,
+// so each lane holds 32 scores of one query), runs the online softmax in fp32
+// with exp2, and accumulates O^T += V^T P^T.  The P fragment is the S fragment
+// converted to bf16 in place: within a 16-key MFMA step, lane half kh supplies
+// keys {4kh..4kh+3, 8+4kh..8+4kh+3}, and the V^T operand is read with the same
+// key order, so P never leaves registers.
+//
+// LDS: K tile [64 keys][64 d] with 16-byte chunks XOR-swizzled by (row>>1)&7;
+// V^T tile [64 d][64 keys] with 8-byte key quads XOR-swizzled by (d>>1)&15.
+// Both swizzles make the fragment reads conflict-free.  Double buffered.
+GPT2_DEV int vt_swz(int d) { return (d >> 1) & 15; }
 
 __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __restrict__ q,
                                                                 KvView kv, bf16_t* __restrict__ o,
                                                                 int H, int T, int l_past, int nqb) {
   constexpr int D = 64;
-  __shared__ uint4 ks[2][64 * 8];      // K tile [key][8 chunks], swizzled chunks
-  __shared__ uint32_t vt[2][64 * 32];  // V^T tile [d][32 key pairs]
+  __shared__ uint4 ks[2][64 * 8];      // K tile, 16-byte chunks
+  __shared__ uint2 vt[2][64 * 16];     // V^T tile, 8-byte key quads
 
   const int qb = nqb - 1 - (int)blockIdx.y;  // longest rows first
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh - (bh / H) * H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
+  const int l32 = lane & 31, kh = lane >> 5;
 
   const int q0 = qb * 128;
-  const int qw0 = q0 + wave * 32;                     // this wave's first query (relative)
-  const int kend = l_past + min(q0 + 128, T);         // keys needed by the workgroup
+  const int qw0 = q0 + wave * 32;                       // this wave's first query (relative)
+  const int kend = l_past + min(q0 + 128, T);           // keys needed by the workgroup
   const int nkb = (kend + 63) / 64;
   const int wave_last = l_past + min(qw0 + 31, T - 1);  // last position this wave needs
+  const int qpos = l_past + qw0 + l32;                  // this lane's query position
 
   const bf16_t* kbase = (const bf16_t*)kv.base + b * kv.sb + h * kv.sh;
   const bf16_t* vbase = kbase + kv.skv;
   const bf16_t* qbase = q + (long long)bh * T * D;
 
-  // Q fragments (MFMA B operand): query qw0 + qt*16 + l16, dims ds*32 + 8g .. +7
-  bf16x8_t qf[2][2];
+  // Q^T fragments (MFMA B operand): query qw0 + l32, dims 16*ds + 8*kh .. +7
+  bf16x8_t qf[4];
+  {
+    const int t = min(qw0 + l32, T - 1);
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int t = min(qw0 + qt * 16 + l16, T - 1);
-#pragma unroll
-    for (int ds = 0; ds < 2; ++ds)
-      qf[qt][ds] = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const uint4*>(qbase + (long long)t * D + ds * 32 + 8 * g));
+    for (int ds = 0; ds < 4; ++ds)
+      qf[ds] = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(qbase + (long long)t * D + 16 * ds + 8 * kh));
   }
 
   // loader mapping: K rows tid>>3 (+32), chunk tid&7; V key pair tid>>3, dims 8*(tid&7)
@@ -81,27 +89,26 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
       const int r = lr + 32 * i;
       ks[st][r * 8 + (lc ^ ((r >> 1) & 7))] = rk[i];
     }
-    // transpose the key pair (2*lr, 2*lr+1) x dims 8*lc..8*lc+7 into V^T
+    // transpose keys (2*lr, 2*lr+1) x dims 8*lc..8*lc+7 into V^T
     const uint32_t a[4] = {rv[0].x, rv[0].y, rv[0].z, rv[0].w};
     const uint32_t c[4] = {rv[1].x, rv[1].y, rv[1].z, rv[1].w};
-    const int kq = lr >> 1;          // key quad
-    const int half = lr & 1;         // which pair inside the quad
+    const int kq = lr >> 1, half = lr & 1;
+    uint32_t* vt32 = reinterpret_cast<uint32_t*>(vt[st]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int d = lc * 8 + e;
       const uint32_t lo = (e & 1) ? (a[e >> 1] >> 16) : (a[e >> 1] & 0xFFFFu);
       const uint32_t hi = (e & 1) ? (c[e >> 1] >> 16) : (c[e >> 1] & 0xFFFFu);
-      vt[st][d * 32 + ((kq ^ vt_swz(d)) * 2) + half] = lo | (hi << 16);
+      vt32[(d * 16 + (kq ^ vt_swz(d))) * 2 + half] = lo | (hi << 16);
     }
   };
 
-  f32x4_t oacc[4][2];
+  f32x16_t oacc[2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) oacc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float mrun[2] = {-INFINITY, -INFINITY};
-  float lrun[2] = {0.f, 0.f};
+    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+  float mrun = -INFINITY, lrun = 0.f;
   const float sc = 0.125f * kLog2e;  // 1/sqrt(64), in the log2 domain
 
   gload(0);
@@ -113,82 +120,71 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
     const int st = kb & 1;
     const int key0 = kb * 64;
     if (key0 <= wave_last) {
-      // ---- S^T = K Q^T for 64 keys x 32 queries
-      f32x4_t s[4][2];
+      // ---- S^T for 2 x 32 keys
+      f32x16_t s[2];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int r = kt * 16 + l16;
-        bf16x8_t kf[2];
+      for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-        for (int ds = 0; ds < 2; ++ds) {
-          const int chunk = ds * 4 + g;
-          kf[ds] = __builtin_bit_cast(bf16x8_t, ks[st][r * 8 + (chunk ^ ((r >> 1) & 7))]);
-        }
+        for (int r = 0; r < 16; ++r) s[kk][r] = 0.f;
+        const int row = kk * 32 + l32;
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qf[qt][0], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1], qf[qt][1], acc, 0, 0, 0);
-          s[kt][qt] = acc;
+        for (int ds = 0; ds < 4; ++ds) {
+          const int chunk = 2 * ds + kh;
+          const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, ks[st][row * 8 + (chunk ^ ((row >> 1) & 7))]);
+          s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kk], 0, 0, 0);
         }
       }
-      // ---- mask (diagonal tiles only), online softmax
+      // ---- mask (diagonal tiles only) and online softmax; lane's keys:
+      // key0 + 32*kk + 8*(r/4) + 4*kh + r%4
       const bool need_mask = key0 + 63 > l_past + qw0;
-      bf16x8_t pf[2][2];  // [key half j][qt]
+      float mx = -INFINITY;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const int qpos = l_past + qw0 + qt * 16 + l16;
-        float mx = -INFINITY;
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int r = 0; r < 16; ++r) {
+          float v = s[kk][r] * sc;
+          if (need_mask && key0 + 32 * kk + 8 * (r >> 2) + 4 * kh + (r & 3) > qpos) v = -INFINITY;
+          s[kk][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(mrun, mx);
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+      mrun = mnew;
+      float ls = 0.f;
+      bf16x8_t pf[4];  // 16-key MFMA steps
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float v = s[kt][qt][r] * sc;
-            if (need_mask && key0 + kt * 16 + 4 * g + r > qpos) v = -INFINITY;
-            s[kt][qt][r] = v;
-            mx = fmaxf(mx, v);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(mrun[qt], mx);
-        const float alpha = __builtin_amdgcn_exp2f(mrun[qt] - mnew);
-        mrun[qt] = mnew;
-        float ls = 0.f;
-        float p[4][4];
+      for (int kk = 0; kk < 2; ++kk) {
+        float p[16];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int r = 0; r < 16; ++r) {
+          p[r] = __builtin_amdgcn_exp2f(s[kk][r] - mnew);
+          ls += p[r];
+        }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            p[kt][r] = __builtin_amdgcn_exp2f(s[kt][qt][r] - mnew);
-            ls += p[kt][r];
-          }
-        lrun[qt] = lrun[qt] * alpha + ls;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) oacc[dt][qt][r] *= alpha;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint4 u = make_uint4(pack_bf2(p[2 * j][0], p[2 * j][1]), pack_bf2(p[2 * j][2], p[2 * j][3]),
-                                     pack_bf2(p[2 * j + 1][0], p[2 * j + 1][1]),
-                                     pack_bf2(p[2 * j + 1][2], p[2 * j + 1][3]));
-          pf[j][qt] = __builtin_bit_cast(bf16x8_t, u);
+        for (int hs = 0; hs < 2; ++hs) {
+          const float* pp = p + 8 * hs;
+          pf[2 * kk + hs] = __builtin_bit_cast(
+              bf16x8_t, make_uint4(pack_bf2(pp[0], pp[1]), pack_bf2(pp[2], pp[3]), pack_bf2(pp[4], pp[5]),
+                                   pack_bf2(pp[6], pp[7])));
         }
       }
-      // ---- O^T += V^T P^T
+      lrun = lrun * alpha + ls;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int d = dt * 16 + l16;
-        const uint32_t* vrow = &vt[st][d * 32];
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int kq1 = 8 * j + g, kq2 = 8 * j + 4 + g;
-          const uint2 x1 = *reinterpret_cast<const uint2*>(vrow + (kq1 ^ vt_swz(d)) * 2);
-          const uint2 x2 = *reinterpret_cast<const uint2*>(vrow + (kq2 ^ vt_swz(d)) * 2);
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+      // ---- O^T += V^T P^T over 4 steps of 16 keys
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const int d = db * 32 + l32;
+        const uint2* vrow = &vt[st][d * 16];
+#pragma unroll
+        for (int ksx = 0; ksx < 4; ++ksx) {
+          const uint2 x1 = vrow[(4 * ksx + kh) ^ vt_swz(d)];
+          const uint2 x2 = vrow[(4 * ksx + 2 + kh) ^ vt_swz(d)];
           const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(x1.x, x1.y, x2.x, x2.y));
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt)
-            oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[j][qt], oacc[dt][qt], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ksx], oacc[db], 0, 0, 0);
         }
       }
     }
@@ -196,22 +192,21 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
     __syncthreads();
   }
 
-  // ---- normalise and store O [B, T, H*64]
+  // ---- normalise and store O [B, T, H*64]; lane holds query qw0 + l32 and
+  // dims 32*db + 8*(r/4) + 4*kh + r%4
+  float l = lrun + __shfl_xor(lrun, 32, 64);
+  const float inv = 1.0f / l;
+  const int t = qw0 + l32;
+  if (t < T) {
+    bf16_t* orow = o + ((long long)b * T + t) * (H * D) + h * D;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    float l = lrun[qt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const float inv = 1.0f / l;
-    const int t = qw0 + qt * 16 + l16;
-    if (t < T) {
-      bf16_t* orow = o + ((long long)b * T + t) * (H * D) + h * D;
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const f32x4_t v = oacc[dt][qt];
-        store4(orow + dt * 16 + 4 * g, make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv));
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x16_t& v = oacc[db];
+        store4(orow + db * 32 + 8 * g4 + 4 * kh,
+               make_float4(v[4 * g4] * inv, v[4 * g4 + 1] * inv, v[4 * g4 + 2] * inv, v[4 * g4 + 3] * inv));
       }
-    }
   }
 }
 
@@ -417,11 +412,15 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float* _
   o[(long long)b * H * D + h * D + lane] = f2bf(acc / L);
 }
 
-void launch_attn_decode_bf16(const bf16_t* q, KvView kv, bf16_t* o, float* part, int B, int H,
-                             int l_past, hipStream_t s) {
+void launch_attn_decode_split(const bf16_t* q, KvView kv, float* part, int B, int H, int l_past,
+                              hipStream_t s) {
   const int nk = l_past + 1;
   const int ns = (nk + kDecKeys - 1) / kDecKeys;
   attn_decode_bf16_kernel<<<dim3(B * H, ns), 256, 0, s>>>(q, kv, part, H, nk, ns);
+}
+
+void launch_attn_decode_combine(const float* part, bf16_t* o, int B, int H, int l_past, hipStream_t s) {
+  const int ns = (l_past + 1 + kDecKeys - 1) / kDecKeys;
   attn_decode_combine_kernel<<<(B * H + 3) / 4, 256, 0, s>>>(part, o, B * H, H, ns);
 }
 

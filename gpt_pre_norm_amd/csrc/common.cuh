@@ -59,11 +59,34 @@ GPT2_DEV float wave_max(float v) {
   return v;
 }
 
+// GELU, tanh approximation: 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
+// Evaluated through the identity 1 + tanh(u) = 2 / (1 + exp(-2u)), i.e.
+// x / (1 + 2^(-2u log2 e)), with the hardware exp2 and reciprocal (about 1 ulp
+// each).  Large |u| saturates correctly: exp2 -> inf gives 0, exp2 -> 0 gives x.
 GPT2_DEV float gelu_tanh(float x) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
   const float k1 = 0.044715f;
-  return 0.5f * x * (1.0f + tanhf(k0 * (x + k1 * x * x * x)));
+  const float m2log2e = -2.0f * 1.4426950408889634f;
+  const float u = k0 * x * fmaf(k1, x * x, 1.0f);
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m2log2e * u));
 }
+
+// Unsigned division by a run-time constant d >= 1 with a precomputed
+// multiplier (round-up method): n / d = (umulhi(n, mul) + n) >> shift for
+// every 31-bit n.
+struct FastDiv {
+  uint32_t mul, shift, d;
+  static FastDiv make(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    f.shift = s;
+    f.mul = (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1);
+    return f;
+  }
+  GPT2_DEV uint32_t div(uint32_t n) const { return (__umulhi(n, mul) + n) >> shift; }
+};
 
 // Strided view of a K/V store: element (b, kv, h, pos, j) lives at
 //   base + b*sb + kv*skv + h*sh + pos*d_h + j

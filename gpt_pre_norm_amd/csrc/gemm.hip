@@ -18,8 +18,13 @@ namespace gpt2 {
 
 // ================================================================ epilogues
 struct EpiStoreF32 {
+  // Rows of the fp32 head output are only 4-byte aligned (N = n_vocab is odd),
+  // so the MFMA kernel hands this epilogue one value per lane with 32
+  // consecutive lanes on one row (row_store), which coalesces dword stores.
+  static constexpr bool kRowStore = true;
   float* out;
   int N;
+  GPT2_DEV void store1(int m, int n, float v) const { out[(long long)m * N + n] = v; }
   GPT2_DEV void operator()(int m, int n, f32x4_t v) const {
     float* p = out + (long long)m * N + n;
     if (n + 3 < N) {
@@ -66,14 +71,15 @@ struct EpiQKV {
   Tact* q;
   KvView kv;
   int T, l_past, H, dh, d;
+  FastDiv divT, divDh;
   GPT2_DEV void operator()(int m, int n, f32x4_t v) const {
     const float4 b = load4(bias + n);
     const float4 y = make_float4(v[0] + b.x, v[1] + b.y, v[2] + b.z, v[3] + b.w);
-    const int sec = n / d;
+    const int sec = (n >= d) + (n >= 2 * d);
     const int c = n - sec * d;
-    const int h = c / dh;
+    const int h = (int)divDh.div((uint32_t)c);
     const int j = c - h * dh;
-    const int bi = m / T;
+    const int bi = (int)divT.div((uint32_t)m);
     const int t = m - bi * T;
     Tact* dst;
     if (sec == 0)
@@ -222,8 +228,213 @@ static void dispatch_bf16(const bf16_t* X, const bf16_t* W, int M, int N, int K,
                           hipStream_t s) {
   if (M <= 64)
     run_bf16<64, 64>(X, W, M, N, K, epi, s);
+  else if (K % 64 == 0)
+    run_bf16_v2<128, 192, 64, 2>(X, W, M, N, K, epi, s);
   else
     run_bf16<128, 128>(X, W, M, N, K, epi, s);
+}
+
+// ================================================================ bf16 MFMA kernel, deep pipeline
+// 32x32x16 MFMA (twice the throughput of 16x16x32 on gfx950), 2x2 waves of
+// (BM/2)x(BN/2), K step BK (32 or 64).  Tiles move global -> LDS with
+// global_load_lds_dwordx4 (no register staging) through a ring of STAGES
+// buffers, issued STAGES-1 K steps ahead; one barrier per K step.  A wave's
+// 64-lane load fills 1 KB of LDS (1024/(2*BK) tile rows), and each lane picks
+// the global 16-byte chunk that the XOR swizzle puts in its slot, so the
+// fragment reads (16 lanes = 16 rows of one chunk) touch all 64 banks once.
+// Requires K % BK == 0.
+template <int BM, int BN, int BK, int STAGES>
+struct V2Cfg {
+  static constexpr int CH = BK / 8;                  // 16-byte chunks per row
+  static constexpr int RPL = 64 / CH;                // rows per wave load (1 KB)
+  static constexpr int SWZ_SHIFT = BK == 64 ? 1 : 2; // rows sharing a bank phase
+  static constexpr int ROWS = BM + BN;               // X rows then W rows
+  static constexpr int GROUPS = ROWS / RPL;          // wave loads per stage
+  static constexpr int LOADS = GROUPS / 4;           // per wave per stage
+  static constexpr int STAGE_U4 = ROWS * CH;         // uint4 per stage
+  static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_U4 * 16;
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(GROUPS % 4 == 0, "row groups must split evenly over 4 waves");
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "wave tiles are multiples of 32");
+  static GPT2_DEV int swz(int row, int c) { return c ^ ((row >> SWZ_SHIFT) & (CH - 1)); }
+};
+
+template <class Epi>
+constexpr bool row_store() {
+  if constexpr (requires { Epi::kRowStore; }) return Epi::kRowStore;
+  else return false;
+}
+
+template <int N>
+GPT2_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Waits until at most `ahead` later stages of this wave's loads are in flight.
+template <int LOADS, int MAXAHEAD>
+GPT2_DEV void wait_stage(int ahead) {
+  if constexpr (MAXAHEAD >= 3) {
+    if (ahead >= 3) { wait_vmcnt<3 * LOADS>(); return; }
+  }
+  if constexpr (MAXAHEAD >= 2) {
+    if (ahead >= 2) { wait_vmcnt<2 * LOADS>(); return; }
+  }
+  if constexpr (MAXAHEAD >= 1) {
+    if (ahead >= 1) { wait_vmcnt<LOADS>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+template <int BM, int BN, int BK, int STAGES, class Epi>
+__global__ __launch_bounds__(256) void gemm_bf16_v2_kernel(const bf16_t* __restrict__ X,
+                                                           const bf16_t* __restrict__ W, int M, int N,
+                                                           int K, Epi epi, int tiles_m, int tiles_n) {
+  using C = V2Cfg<BM, BN, BK, STAGES>;
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int KS = BK / 16;  // MFMA steps per stage
+  extern __shared__ uint4 lds[];
+
+  int tm_idx, tn_idx;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm_idx, tn_idx);
+  const int m0 = tm_idx * BM, n0 = tn_idx * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // this lane's source row / chunk for each of its wave's row groups
+  const bf16_t* src[C::LOADS];
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int g = wave + 4 * i;
+    const int row = C::RPL * g + lane / C::CH;
+    const int c = C::swz(row, lane % C::CH);
+    const bf16_t* base = row < BM ? X + (long long)min(m0 + row, M - 1) * K
+                                  : W + (long long)min(n0 + row - BM, N - 1) * K;
+    src[i] = base + c * 8;
+  }
+  auto issue = [&](int kt, int stage) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int g = wave + 4 * i;
+      uint4* dst = lds + stage * C::STAGE_U4 + g * 64;
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + k0),
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
+  };
+
+  f32x16_t acc[FN][FM];
+#pragma unroll
+  for (int a = 0; a < FN; ++a)
+#pragma unroll
+    for (int b = 0; b < FM; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  const int nk = K / BK;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s, s);
+
+  const int r32 = lane & 31, khalf = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    // wait for this wave's loads of tile kt; later tiles stay in flight
+    wait_stage<C::LOADS, STAGES - 2>(min(STAGES - 2, nk - 1 - kt));
+    __syncthreads();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    const uint4* st = lds + (kt % STAGES) * C::STAGE_U4;
+    // Fragments are double-buffered in registers: the LDS reads of step ks+1
+    // are issued before the MFMAs of step ks, and scheduling barriers keep the
+    // compiler from sinking them next to their uses.
+    bf16x8_t xf[2][FM], wf[2][FN];
+    auto ldfrag = [&](int buf, int ks) {
+      const int chunk = 2 * ks + khalf;
+#pragma unroll
+      for (int f = 0; f < FM; ++f) {
+        const int row = wm * WM + f * 32 + r32;
+        xf[buf][f] = __builtin_bit_cast(bf16x8_t, st[row * C::CH + C::swz(row, chunk)]);
+      }
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        const int row = BM + wn * WN + f * 32 + r32;
+        wf[buf][f] = __builtin_bit_cast(bf16x8_t, st[row * C::CH + C::swz(row, chunk)]);
+      }
+    };
+    ldfrag(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) ldfrag((ks + 1) & 1, ks + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int a = 0; a < FN; ++a)
+#pragma unroll
+        for (int b = 0; b < FM; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][a], xf[ks & 1][b], acc[a][b], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Epilogue through LDS (the patch is wave-private and LDS executes a wave's
+  // accesses in order, so no wait is needed between its write and read-back).
+  // A C[n][m] fragment holds, per lane, column m = r32
+  // and rows n = 8*(r/4) + 4*khalf + r%4: stored directly that is 32 rows x 16 B
+  // per instruction.  Each wave instead writes one 32x32 fragment at a time to
+  // its own LDS patch as [m][n] (row pitch 36 floats) and reads it back with 8
+  // lanes per row, so every epilogue access covers 8 rows x 32 consecutive columns.
+  __syncthreads();  // all waves are done reading the K stages
+  float* patch = reinterpret_cast<float*>(lds) + wave * (32 * 36);
+  const int er = lane >> 3;        // row within an 8-row group
+  const int ec = (lane & 7) * 4;   // first of 4 columns
+#pragma unroll
+  for (int a = 0; a < FN; ++a) {
+#pragma unroll
+    for (int b = 0; b < FM; ++b) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(patch + r32 * 36 + 8 * q + 4 * khalf) =
+            make_float4(acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
+      if constexpr (row_store<Epi>()) {
+        const int n = n0 + wn * WN + a * 32 + r32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 2 * i + khalf;
+          const float v = patch[row * 36 + r32];
+          const int m = m0 + wm * WM + b * 32 + row;
+          if (m < M && n < N) epi.store1(m, n, v);
+        }
+      } else {
+        f32x4_t v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 t = *reinterpret_cast<const float4*>(patch + (8 * i + er) * 36 + ec);
+          v[i] = f32x4_t{t.x, t.y, t.z, t.w};
+        }
+        const int n = n0 + wn * WN + a * 32 + ec;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + wm * WM + b * 32 + 8 * i + er;
+          if (m < M && n < N) epi(m, n, v[i]);
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int BK, int STAGES, class Epi>
+static void run_bf16_v2(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
+                        hipStream_t s) {
+  using C = V2Cfg<BM, BN, BK, STAGES>;
+  static bool attr_set = false;  // one-time, per template instance
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void*)gemm_bf16_v2_kernel<BM, BN, BK, STAGES, Epi>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
+    attr_set = true;
+  }
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  gemm_bf16_v2_kernel<BM, BN, BK, STAGES, Epi><<<tiles_m * tiles_n, 256, C::LDS_BYTES, s>>>(
+      X, W, M, N, K, epi, tiles_m, tiles_n);
 }
 
 // ================================================================ fp32 FMA kernel
@@ -308,7 +519,8 @@ static void launch_typed(const Tact* X, const Tact* W, int M, int N, int K, cons
         go(EpiBiasResid<Tact, Tact, Tact>{(const Tact*)e.bias, (const Tact*)e.resid, (Tact*)e.out, N});
       break;
     case EPI_QKV:
-      go(EpiQKV<Tact>{(const Tact*)e.bias, (Tact*)e.q, e.kv, e.T, e.l_past, e.n_head, e.d_head, e.d});
+      go(EpiQKV<Tact>{(const Tact*)e.bias, (Tact*)e.q, e.kv, e.T, e.l_past, e.n_head, e.d_head, e.d,
+                      FastDiv::make(e.T), FastDiv::make(e.d_head)});
       break;
   }
 }

@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <vector>
 
 #include "../../include/gpt2mi.h"
 #include "kernels.h"
@@ -91,6 +92,52 @@ gpt2_status check_common(const gpt2_hparams& hp, gpt2_mode mode, int B, int T, i
 
 gpt2_status hip_status() { return hipGetLastError() == hipSuccess ? GPT2_OK : GPT2_E_HIP; }
 
+// ---------------------------------------------------------------- kernel timing
+// Between gpt2_timing_begin and gpt2_timing_end every launch is bracketed by
+// a HIP event pair on its stream; events are created once and reused.
+enum Kern {
+  K_EMBED, K_LAYERNORM, K_GEMM_C_ATTN, K_GEMM_ATTN_PROJ, K_GEMM_C_FC, K_GEMM_MLP_PROJ, K_GEMM_HEAD,
+  K_ATTN_PREFILL, K_ATTN_ROWS, K_ATTN_DEC_SPLIT, K_ATTN_DEC_COMBINE, K_COUNT
+};
+const char* const kKernNames[K_COUNT] = {
+    "embed", "layernorm", "gemm_c_attn", "gemm_attn_c_proj", "gemm_c_fc", "gemm_mlp_c_proj",
+    "gemm_lm_head", "attn_prefill", "attn_rows_f32", "attn_decode_split", "attn_decode_combine"};
+
+struct Timing {
+  bool on = false;
+  bool failed = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<int> kinds;  // one per recorded pair
+  size_t used = 0;         // events taken from the pool in this session
+
+  hipEvent_t take() {
+    if (used == pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) {
+        failed = true;
+        return nullptr;
+      }
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+};
+Timing g_timing;
+
+// Runs launch() on stream s, bracketed by an event pair when timing is on.
+template <class F>
+void timed(int kind, hipStream_t s, F&& launch) {
+  if (!g_timing.on) {
+    launch();
+    return;
+  }
+  hipEvent_t a = g_timing.take(), b = g_timing.take();
+  if (a) hipEventRecord(a, s);
+  launch();
+  if (b) hipEventRecord(b, s);
+  g_timing.kinds.push_back(kind);
+}
+
 struct Run {
   const gpt2_hparams& hp;
   gpt2_mode mode;
@@ -116,7 +163,7 @@ struct Run {
     void* o = at(L.o);
     void* u = at(L.u);
     // LN1
-    launch_layernorm(x_in_f32 || !b16, b16, x_in, w.ln1_g, w.ln1_b, a, m, d, hp.eps, s);
+    timed(K_LAYERNORM, s, [&] { launch_layernorm(x_in_f32 || !b16, b16, x_in, w.ln1_g, w.ln1_b, a, m, d, hp.eps, s); });
     // c_attn: q to [B,H,T,dh], k/v into the view at positions l_past..
     Epilogue e{};
     e.kind = EPI_QKV;
@@ -128,14 +175,17 @@ struct Run {
     e.n_head = H;
     e.d_head = dh;
     e.d = d;
-    launch_gemm(b16, a, w.attn_w, m, 3 * d, d, e, s);
+    timed(K_GEMM_C_ATTN, s, [&] { launch_gemm(b16, a, w.attn_w, m, 3 * d, d, e, s); });
     // causal attention -> o [B, T, d]
-    if (!b16)
-      launch_attn_rows_f32((const float*)q, kv, (float*)o, B, H, T, dh, l_past, s);
-    else if (decode)
-      launch_attn_decode_bf16((const bf16_t*)q, kv, (bf16_t*)o, (float*)at(L.part), B, H, l_past, s);
-    else
-      launch_attn_prefill_bf16((const bf16_t*)q, kv, (bf16_t*)o, B, H, T, l_past, s);
+    if (!b16) {
+      timed(K_ATTN_ROWS, s, [&] { launch_attn_rows_f32((const float*)q, kv, (float*)o, B, H, T, dh, l_past, s); });
+    } else if (decode) {
+      float* part = (float*)at(L.part);
+      timed(K_ATTN_DEC_SPLIT, s, [&] { launch_attn_decode_split((const bf16_t*)q, kv, part, B, H, l_past, s); });
+      timed(K_ATTN_DEC_COMBINE, s, [&] { launch_attn_decode_combine(part, (bf16_t*)o, B, H, l_past, s); });
+    } else {
+      timed(K_ATTN_PREFILL, s, [&] { launch_attn_prefill_bf16((const bf16_t*)q, kv, (bf16_t*)o, B, H, T, l_past, s); });
+    }
     // c_proj + bias + residual -> x1 (fp32)
     Epilogue p{};
     p.kind = EPI_BIAS_RESID;
@@ -144,14 +194,14 @@ struct Run {
     p.resid_f32 = x_in_f32 || !b16;
     p.out = x1;
     p.out_f32 = true;
-    launch_gemm(b16, o, w.proj_w, m, d, d, p, s);
+    timed(K_GEMM_ATTN_PROJ, s, [&] { launch_gemm(b16, o, w.proj_w, m, d, d, p, s); });
     // LN2, c_fc + GELU
-    launch_layernorm(true, b16, x1, w.ln2_g, w.ln2_b, a, m, d, hp.eps, s);
+    timed(K_LAYERNORM, s, [&] { launch_layernorm(true, b16, x1, w.ln2_g, w.ln2_b, a, m, d, hp.eps, s); });
     Epilogue f{};
     f.kind = EPI_BIAS_GELU;
     f.bias = w.fc_b;
     f.out = u;
-    launch_gemm(b16, a, w.fc_w, m, 4 * d, d, f, s);
+    timed(K_GEMM_C_FC, s, [&] { launch_gemm(b16, a, w.fc_w, m, 4 * d, d, f, s); });
     // mlp.c_proj + bias + residual -> y
     Epilogue f2{};
     f2.kind = EPI_BIAS_RESID;
@@ -160,7 +210,7 @@ struct Run {
     f2.resid_f32 = true;
     f2.out = y;
     f2.out_f32 = y_f32 || !b16;
-    launch_gemm(b16, u, w.fc2_w, m, d, 4 * d, f2, s);
+    timed(K_GEMM_MLP_PROJ, s, [&] { launch_gemm(b16, u, w.fc2_w, m, d, 4 * d, f2, s); });
   }
 
   // Cache [B, n_layer, 2, H, cap, dh] viewed at one layer.
@@ -190,17 +240,17 @@ struct Run {
     const int d = hp.n_embd, m = M();
     const bool b16 = bf16();
     float* x = (float*)at(L.x);
-    launch_embed(b16, ids, W.wte, W.wpe, x, m, T, l_past, d, hp.n_vocab, (uint32_t*)ws, s);
+    timed(K_EMBED, s, [&] { launch_embed(b16, ids, W.wte, W.wpe, x, m, T, l_past, d, hp.n_vocab, (uint32_t*)ws, s); });
     for (int l = 0; l < hp.n_layer; ++l) {
       const KvView kv = cache ? cache_view(cache->data, cache->capacity, l) : present_view(at(L.kv));
       block(W.blocks[l], x, true, x, x, true, kv);
     }
     void* a = at(L.a);
-    launch_layernorm(true, b16, x, W.lnf_g, W.lnf_b, a, m, d, hp.eps, s);
+    timed(K_LAYERNORM, s, [&] { launch_layernorm(true, b16, x, W.lnf_g, W.lnf_b, a, m, d, hp.eps, s); });
     Epilogue e{};
     e.kind = EPI_STORE_F32;
     e.out = logits;
-    launch_gemm(b16, a, W.wte, m, hp.n_vocab, d, e, s);
+    timed(K_GEMM_HEAD, s, [&] { launch_gemm(b16, a, W.wte, m, hp.n_vocab, d, e, s); });
   }
 };
 
@@ -287,6 +337,41 @@ gpt2_status gpt2_read_device_flags(void* ws, void* stream) {
   if (hipMemset(ws, 0, sizeof(flags)) != hipSuccess) return GPT2_E_HIP;
   if (hipDeviceSynchronize() != hipSuccess) return GPT2_E_HIP;
   return GPT2_E_TOKEN;
+}
+
+gpt2_status gpt2_timing_begin(void) {
+  g_timing.on = true;
+  g_timing.failed = false;
+  g_timing.used = 0;
+  g_timing.kinds.clear();
+  return GPT2_OK;
+}
+
+int32_t gpt2_timing_end(gpt2_kernel_time* out, int32_t max_entries) {
+  if (!g_timing.on) return -1;
+  g_timing.on = false;
+  if (g_timing.failed) return -1;
+  double total[K_COUNT] = {};
+  int count[K_COUNT] = {};
+  for (size_t i = 0; i < g_timing.kinds.size(); ++i) {
+    hipEvent_t a = g_timing.pool[2 * i], b = g_timing.pool[2 * i + 1];
+    if (hipEventSynchronize(b) != hipSuccess) return -1;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, a, b) != hipSuccess) return -1;
+    total[g_timing.kinds[i]] += ms;
+    count[g_timing.kinds[i]] += 1;
+  }
+  int32_t n = 0;
+  for (int k = 0; k < K_COUNT; ++k) {
+    if (count[k] == 0) continue;
+    if (out && n < max_entries) {
+      out[n].name = kKernNames[k];
+      out[n].launches = count[k];
+      out[n].total_ms = total[k];
+    }
+    ++n;
+  }
+  return n;
 }
 
 }  // extern "C"

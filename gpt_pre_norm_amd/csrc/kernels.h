@@ -61,7 +61,8 @@ void launch_attn_rows_f32(const float* q, KvView kv, float* o, int B, int H, int
 // Single-token decode (bf16, d_h == 64): split over keys + combine.
 // part: workspace of decode_part_floats(B, H, l_past) floats.
 size_t decode_part_floats(int B, int H, int n_keys);
-void launch_attn_decode_bf16(const bf16_t* q, KvView kv, bf16_t* o, float* part, int B, int H,
-                             int l_past, hipStream_t s);
+void launch_attn_decode_split(const bf16_t* q, KvView kv, float* part, int B, int H, int l_past,
+                              hipStream_t s);
+void launch_attn_decode_combine(const float* part, bf16_t* o, int B, int H, int l_past, hipStream_t s);
 
 }  // namespace gpt2

@@ -20,7 +20,7 @@ FP32, BF16 = 0, 1
 STATUS = {0: "GPT2_OK", 1: "GPT2_E_NULL", 2: "GPT2_E_SHAPE", 3: "GPT2_E_DTYPE",
           4: "GPT2_E_POSITION", 5: "GPT2_E_WORKSPACE", 6: "GPT2_E_TOKEN", 7: "GPT2_E_HIP"}
 EXPORTS = ("gpt2_workspace_size", "gpt2_block_forward", "gpt2_forward", "gpt2_decode_step",
-           "gpt2_read_device_flags", "gpt2_status_str")
+           "gpt2_read_device_flags", "gpt2_timing_begin", "gpt2_timing_end", "gpt2_status_str")
 BLOCK_KEYS = ("ln1_g", "ln1_b", "attn_w", "attn_b", "proj_w", "proj_b",
               "ln2_g", "ln2_b", "fc_w", "fc_b", "fc2_w", "fc2_b")
 
@@ -49,6 +49,10 @@ class KV(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("capacity", ctypes.c_int32)]
 
 
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
+
+
 _lib = None
 
 
@@ -71,6 +75,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gpt2_decode_step.argtypes = [hp_p, ctypes.c_int, ctypes.POINTER(Weights), vp, i32, i32,
                                      ctypes.POINTER(KV), vp, vp, sz, vp]
     lib.gpt2_read_device_flags.argtypes = [vp, vp]
+    lib.gpt2_timing_begin.argtypes = []
+    lib.gpt2_timing_begin.restype = ctypes.c_int
+    lib.gpt2_timing_end.argtypes = [ctypes.POINTER(KernelTime), i32]
+    lib.gpt2_timing_end.restype = i32
     lib.gpt2_status_str.argtypes = [ctypes.c_int]
     lib.gpt2_status_str.restype = ctypes.c_char_p
     for f in ("gpt2_block_forward", "gpt2_forward", "gpt2_decode_step", "gpt2_read_device_flags"):
@@ -180,6 +188,19 @@ def decode_step(hp: HParams, mode: int, W: ModelWeights, ids, B: int, l_past: in
 def read_device_flags(ws, stream=None) -> int:
     """Returns the status (0 or GPT2_E_TOKEN) and clears the flags."""
     return int(load().gpt2_read_device_flags(_ptr(ws), _stream(stream)))
+
+
+def timing_begin() -> None:
+    _check(load().gpt2_timing_begin(), "gpt2_timing_begin")
+
+
+def timing_end() -> dict:
+    """{kernel name: (launches, total ms)} for the launches since timing_begin()."""
+    buf = (KernelTime * 32)()
+    n = load().gpt2_timing_end(buf, 32)
+    if n < 0:
+        raise Gpt2Error(7, "gpt2_timing_end")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n, 32))}
 
 
 def status_str(st: int) -> str:

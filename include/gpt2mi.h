@@ -130,6 +130,24 @@ gpt2_status gpt2_decode_step(const gpt2_hparams *hp, gpt2_mode mode, const gpt2_
  * outside [0, n_vocab), else GPT2_OK (or GPT2_E_HIP). */
 gpt2_status gpt2_read_device_flags(void *ws, void *stream);
 
+/* Per-kernel timing, for measurement only (the compute path never needs it).
+ * After gpt2_timing_begin(), every kernel that the compute calls enqueue is
+ * bracketed by a HIP event pair recorded on the call's stream; the events
+ * are host-side objects the library creates once and reuses (no device
+ * memory).  gpt2_timing_end() waits for the last event, sums the elapsed time
+ * per kernel kind, writes at most max_entries records to `out` (name: static
+ * string such as "gemm_c_fc" or "attn_decode_split") and returns the number
+ * of kinds seen, or -1 if timing was not on or a HIP call failed.  Not
+ * thread-safe: one timing session per process at a time. */
+typedef struct {
+  const char *name;
+  int32_t launches;
+  double total_ms;
+} gpt2_kernel_time;
+
+gpt2_status gpt2_timing_begin(void);
+int32_t gpt2_timing_end(gpt2_kernel_time *out, int32_t max_entries);
+
 /* Static, human-readable name of a status code. */
 const char *gpt2_status_str(gpt2_status s);
 

@@ -208,18 +208,30 @@ def bench_decode(args, G, R, synth, wl, Wd, hp, stream, dev):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.decode_steps):
-        step()
-    ev1.record(stream)
+
+    def timed_loop(fn, n):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record()
+        for _ in range(n):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return max((time.perf_counter() - t0) * 1e3, ev0.elapsed_time(ev1)) / n
+
+    ms_eager = timed_loop(step, args.decode_steps)
+    # the same step captured once into a HIP graph and replayed (the ~100
+    # launches of a step are what the graph saves; the kernels are identical)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        G.decode_step(hp, G.BF16, Wd, ids, wl.B, wl.l_past, cache, cap, logits, ws=ws)
+    graph.replay()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = max(wall * 1e3, ev0.elapsed_time(ev1)) / args.decode_steps
+    ms = timed_loop(graph.replay, args.decode_steps)
     byt = R.decode_bytes(wl.B, wl.d, wl.h, wl.L, wl.n_vocab, wl.l_past)
-    log(f"[bench] decode {ms * 1e3:.1f} us/step, {wl.B / (ms / 1e3):.4g} tok/s, "
-        f"{byt / (ms / 1e3) / 1e9:.0f} GB/s algorithmic")
+    log(f"[bench] decode eager {ms_eager * 1e3:.1f} us/step; graph {ms * 1e3:.1f} us/step, "
+        f"{wl.B / (ms / 1e3):.4g} tok/s, {byt / (ms / 1e3) / 1e9:.0f} GB/s algorithmic")
     G.timing_begin()
     for _ in range(args.decode_steps):
         step()
@@ -241,7 +253,8 @@ def bench_decode(args, G, R, synth, wl, Wd, hp, stream, dev):
     ach = b / avg_s / 1e9
     return {
         "value": round(wl.B / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
-        "steps": args.decode_steps,
+        "steps": args.decode_steps, "launch": "hip graph replay of one decode step",
+        "ms_per_step_eager": round(ms_eager, 4),
         "workload": "GPT-2 small cached decode, bf16, B=64, one new token at position 1023, "
                     "past [64,12,2,12,1023,64] ~ N(0,1)",
         "hbm_frac_whole_step": round(byt / (ms / 1e3) / R.PEAK_HBM_BYTES, 4),

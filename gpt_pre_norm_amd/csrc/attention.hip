@@ -13,9 +13,9 @@
 //    are skipped by that wave; only diagonal tiles apply the mask.
 //  * attn_rows_f32: one wave per query row with a full (max-subtracted)
 //    softmax, for the fp32 mode.
-//  * attn_decode_bf16: one new query per (sequence, head) streaming the cache;
-//    the keys are split over workgroups, each writes (max, sum, unnormalised
-//    output) and a combine kernel merges the splits.
+//  * attn_decode_bf16: one new query per (sequence, head) streaming the cache
+//    with one 16-wave workgroup per (sequence, head); the waves' online
+//    softmax states merge in LDS.
 #include "kernels.h"
 
 namespace gpt2 {
@@ -288,86 +288,86 @@ void launch_attn_rows_f32(const float* q, KvView kv, float* o, int B, int H, int
 }
 
 // ================================================================ decode (bf16, d_h = 64)
-static constexpr int kDecKeys = 256;  // keys per workgroup (64 per wave)
-static constexpr int kPart = 64 + 2;  // partial record: max, sum, out[64]
+// One workgroup of 16 waves per (sequence, head) streams the whole cache row
+// range 0 .. l_past: wave w takes keys w*64 + 1024*j.  Inside a wave, 8 lanes
+// share a key row (8 dims each) and 8 rows are in flight per pass; a lane
+// issues its 8 K and 8 V row loads together (256 KB in flight per workgroup).
+// Each wave keeps an online softmax (running max, partial sums per lane);
+// the 16 waves then merge through LDS, so no second kernel is needed.
+static constexpr int kDecWaves = 16;
 
-size_t decode_part_floats(int B, int H, int n_keys) {
-  const int ns = (n_keys + kDecKeys - 1) / kDecKeys;
-  return (size_t)B * H * ns * kPart;
-}
-
-// Lane layout inside a wave: 8 lanes per key row (8 dims each), 8 rows per
-// pass, 8 passes = 64 keys; all 16 row loads of a lane are issued together.
-__global__ __launch_bounds__(256) void attn_decode_bf16_kernel(const bf16_t* __restrict__ q, KvView kv,
-                                                               float* __restrict__ part, int H,
-                                                               int nk, int ns) {
+__global__ __launch_bounds__(1024) void attn_decode_bf16_kernel(const bf16_t* __restrict__ q, KvView kv,
+                                                                bf16_t* __restrict__ o, int H, int nk) {
   constexpr int D = 64;
-  __shared__ float wmax[4];
-  __shared__ float wsum[4];
-  __shared__ float wout[4][D];
-  const int split = blockIdx.y, bh = blockIdx.x;
+  __shared__ float wm[kDecWaves];
+  __shared__ float wl[kDecWaves];
+  __shared__ float wo[kDecWaves][D];
+  const int bh = blockIdx.x;
   const int b = bh / H, h = bh - (bh / H) * H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c8 = lane & 7, rg = lane >> 3;
 
   const bf16_t* kbase = (const bf16_t*)kv.base + b * kv.sb + h * kv.sh;
   const bf16_t* vbase = kbase + kv.skv;
-  const int key0 = split * kDecKeys + wave * 64;
-
   const uint4 qu = *reinterpret_cast<const uint4*>(q + (long long)bh * D + c8 * 8);
   const float qv[8] = {bf_lo(qu.x), bf_hi(qu.x), bf_lo(qu.y), bf_hi(qu.y),
                        bf_lo(qu.z), bf_hi(qu.z), bf_lo(qu.w), bf_hi(qu.w)};
-  uint4 kr[8], vr[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int key = min(key0 + rg + 8 * i, nk - 1);
-    kr[i] = *reinterpret_cast<const uint4*>(kbase + (long long)key * D + c8 * 8);
-    vr[i] = *reinterpret_cast<const uint4*>(vbase + (long long)key * D + c8 * 8);
-  }
-  const float sc = 0.125f * kLog2e;
-  float sv[8];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint4 u = kr[i];
-    float acc = qv[0] * bf_lo(u.x);
-    acc = fmaf(qv[1], bf_hi(u.x), acc);
-    acc = fmaf(qv[2], bf_lo(u.y), acc);
-    acc = fmaf(qv[3], bf_hi(u.y), acc);
-    acc = fmaf(qv[4], bf_lo(u.z), acc);
-    acc = fmaf(qv[5], bf_hi(u.z), acc);
-    acc = fmaf(qv[6], bf_lo(u.w), acc);
-    acc = fmaf(qv[7], bf_hi(u.w), acc);
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    acc += __shfl_xor(acc, 4, 64);
-    const int key = key0 + rg + 8 * i;
-    sv[i] = key < nk ? acc * sc : -INFINITY;
-    mx = fmaxf(mx, sv[i]);
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 8, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  if (lane == 0) wmax[wave] = mx;
-  __syncthreads();
-  const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  float l = 0.f;
+  const float sc = 0.125f * kLog2e;  // 1/sqrt(64), in the log2 domain
+
+  float m = -INFINITY, l = 0.f;
   float ov[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int key0 = wave * 64; key0 < nk; key0 += 64 * kDecWaves) {
+    uint4 kr[8], vr[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float p = __builtin_amdgcn_exp2f(sv[i] - m);  // 0 for masked keys
-    l += p;
-    const uint4 u = vr[i];
-    ov[0] = fmaf(p, bf_lo(u.x), ov[0]);
-    ov[1] = fmaf(p, bf_hi(u.x), ov[1]);
-    ov[2] = fmaf(p, bf_lo(u.y), ov[2]);
-    ov[3] = fmaf(p, bf_hi(u.y), ov[3]);
-    ov[4] = fmaf(p, bf_lo(u.z), ov[4]);
-    ov[5] = fmaf(p, bf_hi(u.z), ov[5]);
-    ov[6] = fmaf(p, bf_lo(u.w), ov[6]);
-    ov[7] = fmaf(p, bf_hi(u.w), ov[7]);
+    for (int i = 0; i < 8; ++i) {
+      const int key = min(key0 + rg + 8 * i, nk - 1);
+      kr[i] = *reinterpret_cast<const uint4*>(kbase + (long long)key * D + c8 * 8);
+      vr[i] = *reinterpret_cast<const uint4*>(vbase + (long long)key * D + c8 * 8);
+    }
+    float sv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 u = kr[i];
+      float acc = qv[0] * bf_lo(u.x);
+      acc = fmaf(qv[1], bf_hi(u.x), acc);
+      acc = fmaf(qv[2], bf_lo(u.y), acc);
+      acc = fmaf(qv[3], bf_hi(u.y), acc);
+      acc = fmaf(qv[4], bf_lo(u.z), acc);
+      acc = fmaf(qv[5], bf_hi(u.z), acc);
+      acc = fmaf(qv[6], bf_lo(u.w), acc);
+      acc = fmaf(qv[7], bf_hi(u.w), acc);
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      acc += __shfl_xor(acc, 4, 64);
+      sv[i] = key0 + rg + 8 * i < nk ? acc * sc : -INFINITY;
+      mx = fmaxf(mx, sv[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 8, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(m, mx);  // finite: key0 < nk, so row rg=0, i=0 is a real key
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    m = mnew;
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ov[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = __builtin_amdgcn_exp2f(sv[i] - mnew);  // 0 for masked keys
+      l += p;
+      const uint4 u = vr[i];
+      ov[0] = fmaf(p, bf_lo(u.x), ov[0]);
+      ov[1] = fmaf(p, bf_hi(u.x), ov[1]);
+      ov[2] = fmaf(p, bf_lo(u.y), ov[2]);
+      ov[3] = fmaf(p, bf_hi(u.y), ov[3]);
+      ov[4] = fmaf(p, bf_lo(u.z), ov[4]);
+      ov[5] = fmaf(p, bf_hi(u.z), ov[5]);
+      ov[6] = fmaf(p, bf_lo(u.w), ov[6]);
+      ov[7] = fmaf(p, bf_hi(u.w), ov[7]);
+    }
   }
-  // sum over the 8 row groups (p is replicated over the 8 lanes of a row)
+  // sum the 8 row groups (each key's p is replicated over the 8 lanes of its row)
 #pragma unroll
   for (int off = 8; off < 64; off <<= 1) {
     l += __shfl_xor(l, off, 64);
@@ -376,52 +376,31 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(const bf16_t* __r
   }
   if (lane < 8) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) wout[wave][lane * 8 + e] = ov[e];
+    for (int e = 0; e < 8; ++e) wo[wave][lane * 8 + e] = ov[e];
   }
-  if (lane == 0) wsum[wave] = l;
+  if (lane == 0) {
+    wm[wave] = m;  // -inf for a wave that had no keys
+    wl[wave] = l;
+  }
   __syncthreads();
-  if (tid < D + 2) {
-    float* rec = part + ((long long)bh * ns + split) * kPart;
-    if (tid < D)
-      rec[2 + tid] = (wout[0][tid] + wout[1][tid]) + (wout[2][tid] + wout[3][tid]);
-    else if (tid == D)
-      rec[0] = m;
-    else
-      rec[1] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  if (tid < D) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, wm[w]);
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float f = __builtin_amdgcn_exp2f(wm[w] - M);
+      L = fmaf(wl[w], f, L);
+      acc = fmaf(wo[w][tid], f, acc);
+    }
+    o[(long long)b * H * D + h * D + tid] = f2bf(acc / L);
   }
 }
 
-// One wave per (sequence, head); lane = output dim.
-__global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float* __restrict__ part,
-                                                                  bf16_t* __restrict__ o, int BH, int H,
-                                                                  int ns) {
-  constexpr int D = 64;
-  const int lane = threadIdx.x & 63;
-  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (bh >= BH) return;
-  const float* rec = part + (long long)bh * ns * kPart;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, rec[s * kPart]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = __builtin_amdgcn_exp2f(rec[s * kPart] - M);
-    L = fmaf(rec[s * kPart + 1], w, L);
-    acc = fmaf(rec[s * kPart + 2 + lane], w, acc);
-  }
-  const int b = bh / H, h = bh - (bh / H) * H;
-  o[(long long)b * H * D + h * D + lane] = f2bf(acc / L);
-}
-
-void launch_attn_decode_split(const bf16_t* q, KvView kv, float* part, int B, int H, int l_past,
-                              hipStream_t s) {
-  const int nk = l_past + 1;
-  const int ns = (nk + kDecKeys - 1) / kDecKeys;
-  attn_decode_bf16_kernel<<<dim3(B * H, ns), 256, 0, s>>>(q, kv, part, H, nk, ns);
-}
-
-void launch_attn_decode_combine(const float* part, bf16_t* o, int B, int H, int l_past, hipStream_t s) {
-  const int ns = (l_past + 1 + kDecKeys - 1) / kDecKeys;
-  attn_decode_combine_kernel<<<(B * H + 3) / 4, 256, 0, s>>>(part, o, B * H, H, ns);
+void launch_attn_decode_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int l_past,
+                             hipStream_t s) {
+  attn_decode_bf16_kernel<<<B * H, 64 * kDecWaves, 0, s>>>(q, kv, o, H, l_past + 1);
 }
 
 }  // namespace gpt2

@@ -65,6 +65,33 @@ struct EpiBiasResid {
   }
 };
 
+// In-place fp32 residual update x += acc + bias.  The skinny decode kernel may
+// split K over workgroups; it then calls add(), which accumulates each K
+// range's share with fp32 atomics and adds the bias once (first range).
+template <typename Tact>
+struct EpiResidInPlace {
+  static constexpr bool kAtomicResid = true;
+  const Tact* bias;
+  float* x;
+  int N;
+  GPT2_DEV void operator()(int m, int n, f32x4_t v) const {
+    const float4 b = load4(bias + n);
+    float* p = x + (long long)m * N + n;
+    const float4 r = *reinterpret_cast<const float4*>(p);
+    *reinterpret_cast<float4*>(p) =
+        make_float4(r.x + (v[0] + b.x), r.y + (v[1] + b.y), r.z + (v[2] + b.z), r.w + (v[3] + b.w));
+  }
+  GPT2_DEV void add(int m, int n, f32x4_t v, bool with_bias) const {
+    float* p = x + (long long)m * N + n;
+    float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (with_bias) b = load4(bias + n);
+    unsafeAtomicAdd(p + 0, v[0] + b.x);
+    unsafeAtomicAdd(p + 1, v[1] + b.y);
+    unsafeAtomicAdd(p + 2, v[2] + b.z);
+    unsafeAtomicAdd(p + 3, v[3] + b.w);
+  }
+};
+
 template <typename Tact>
 struct EpiQKV {
   const Tact* bias;
@@ -223,16 +250,6 @@ static void run_bf16(const bf16_t* X, const bf16_t* W, int M, int N, int K, cons
   gemm_bf16_kernel<BM, BN, Epi><<<tiles_m * tiles_n, 256, 0, s>>>(X, W, M, N, K, epi, tiles_m, tiles_n);
 }
 
-template <class Epi>
-static void dispatch_bf16(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
-                          hipStream_t s) {
-  if (M <= 64)
-    run_bf16<64, 64>(X, W, M, N, K, epi, s);
-  else if (K % 64 == 0)
-    run_bf16_v2<128, 192, 64, 2>(X, W, M, N, K, epi, s);
-  else
-    run_bf16<128, 128>(X, W, M, N, K, epi, s);
-}
 
 // ================================================================ bf16 MFMA kernel, deep pipeline
 // 32x32x16 MFMA (twice the throughput of 16x16x32 on gfx950), 2x2 waves of
@@ -437,6 +454,163 @@ static void run_bf16_v2(const bf16_t* X, const bf16_t* W, int M, int N, int K, c
       X, W, M, N, K, epi, tiles_m, tiles_n);
 }
 
+// ================================================================ skinny bf16 kernel (M <= 64)
+// Decode-sized products: each weight byte is used once, so the job is to
+// stream W from HBM with every CU busy and many bytes in flight.  A workgroup
+// owns NT output columns (NT rows of W) and one of S ranges of K (kc = K/S
+// <= 768): it issues every load of its X tile [64 x kc] and W tile [NT x kc]
+// at once with global_load_lds_dwordx4 (coalesced rows, XOR-swizzled 16-byte
+// chunks in LDS), waits once, and its 4 waves split kc for the MFMA
+// v_mfma_f32_16x16x32_bf16 (W rows as the A operand).  The waves' partial sums
+// meet in LDS.  S > 1 is used only for the in-place fp32 residual epilogue,
+// which then adds each K range's share with fp32 atomics (the bias with the
+// first range); every other epilogue runs with S = 1.
+constexpr int kSkinnyMaxKc = 768;
+
+template <class Epi>
+constexpr bool atomic_resid() {
+  if constexpr (requires { Epi::kAtomicResid; }) return Epi::kAtomicResid;
+  else return false;
+}
+
+template <int NT, class Epi>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16_t* __restrict__ X,
+                                                          const bf16_t* __restrict__ W, int M, int N,
+                                                          int K, int S, Epi epi, FastDiv cdiv) {
+  extern __shared__ uint4 lds[];
+  constexpr int ROWS = 64 + NT;  // X rows then W rows
+  constexpr int FN = NT / 16;    // A fragments (W) per step
+  const int ns = blockIdx.x / S, split = blockIdx.x - (blockIdx.x / S) * S;
+  const int n0 = ns * NT;
+  const int kc = K / S, k0 = split * kc;
+  const int cpr = kc / 8;  // 16-byte chunks per row
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // ---- issue the whole tile: slot p of LDS holds (row p / cpr, chunk (p % cpr) ^ (row & 15)).
+  // total is a multiple of 256 (ROWS is 80 or 96, cpr a multiple of 16), so
+  // every 64-slot wave load lies inside the tile.
+  const int total = ROWS * cpr;
+  for (int base = wave * 64; base < total; base += 256) {
+    const int p = base + lane;
+    const int row = (int)cdiv.div((uint32_t)p);
+    const int c = (p - row * cpr) ^ (row & 15);
+    const bf16_t* src = row < 64 ? X + (long long)min(row, M - 1) * K
+                                 : W + (long long)min(n0 + row - 64, N - 1) * K;
+    __builtin_amdgcn_global_load_lds((const void*)(src + k0 + c * 8),
+                                     (__attribute__((address_space(3))) void*)(lds + base), 16, 0, 0);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // ---- MFMA over this wave's quarter of kc
+  f32x4_t acc[FN][4];
+#pragma unroll
+  for (int a = 0; a < FN; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int l16 = lane & 15, kg = lane >> 4;
+  const int steps = kc / 32 / 4;  // 32-wide k steps per wave
+  for (int st = 0; st < steps; ++st) {
+    const int c = (wave * steps + st) * 4 + kg;
+    bf16x8_t wf[FN], xf[4];
+#pragma unroll
+    for (int a = 0; a < FN; ++a) {
+      const int row = 64 + a * 16 + l16;
+      wf[a] = __builtin_bit_cast(bf16x8_t, lds[row * cpr + (c ^ (row & 15))]);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int row = b * 16 + l16;
+      xf[b] = __builtin_bit_cast(bf16x8_t, lds[row * cpr + (c ^ (row & 15))]);
+    }
+#pragma unroll
+    for (int a = 0; a < FN; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[a], xf[b], acc[a][b], 0, 0, 0);
+  }
+  // ---- the 4 waves' partial sums meet in LDS: [wave][FN*4 fragments][64 lanes] float4
+  __syncthreads();
+  float4* red = reinterpret_cast<float4*>(lds);
+#pragma unroll
+  for (int a = 0; a < FN; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      red[(wave * FN * 4 + a * 4 + b) * 64 + lane] =
+          make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+  __syncthreads();
+  // fragment f = tid / 64 (+4): C[n][m] with m = 16*(f%4) + lane%16, n = 16*(f/4) + 4*(lane/16)
+  for (int f = wave; f < FN * 4; f += 4) {
+    float4 v = red[f * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const float4 u = red[(w * FN * 4 + f) * 64 + lane];
+      v = make_float4(v.x + u.x, v.y + u.y, v.z + u.z, v.w + u.w);
+    }
+    const int m = 16 * (f & 3) + l16;
+    const int n = n0 + 16 * (f >> 2) + 4 * kg;
+    if (m < M && n < N) {
+      if constexpr (atomic_resid<Epi>()) {
+        if (S > 1) {
+          epi.add(m, n, f32x4_t{v.x, v.y, v.z, v.w}, split == 0);
+          continue;
+        }
+      }
+      epi(m, n, f32x4_t{v.x, v.y, v.z, v.w});
+    }
+  }
+}
+
+// K ranges for the skinny kernel: the fewest that keep kc = K/S <= 768 with
+// K/S a multiple of 128 (16 chunks per LDS row).  0 if none exists.
+static int skinny_splits(int K) {
+  for (int s = 1; s <= K / 128; ++s)
+    if (K % s == 0 && (K / s) % 128 == 0 && K / s <= kSkinnyMaxKc) return s;
+  return 0;
+}
+
+template <int NT, class Epi>
+static void run_skinny(const bf16_t* X, const bf16_t* W, int M, int N, int K, int S, const Epi& epi,
+                       hipStream_t s) {
+  const size_t lds = (size_t)(64 + NT) * (K / S) * 2;
+  static bool attr_set = false;  // one-time, per template instance
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void*)gemm_skinny_kernel<NT, Epi>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr_set = true;
+  }
+  const int nslices = (N + NT - 1) / NT;
+  gemm_skinny_kernel<NT, Epi><<<nslices * S, 256, lds, s>>>(X, W, M, N, K, S, epi,
+                                                             FastDiv::make((uint32_t)(K / S / 8)));
+}
+
+// Chooses the skinny kernel when it applies; returns false otherwise.
+template <class Epi>
+static bool try_skinny(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
+                       hipStream_t s) {
+  if (M > 64) return false;
+  const int S = skinny_splits(K);
+  if (S == 0 || (S > 1 && !atomic_resid<Epi>())) return false;
+  if (N >= 8192)
+    run_skinny<32>(X, W, M, N, K, S, epi, s);
+  else
+    run_skinny<16>(X, W, M, N, K, S, epi, s);
+  return true;
+}
+
+template <class Epi>
+static void dispatch_bf16(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
+                          hipStream_t s) {
+  if (try_skinny(X, W, M, N, K, epi, s))
+    return;
+  if (M <= 64)
+    run_bf16<64, 64>(X, W, M, N, K, epi, s);
+  else if (K % 64 == 0)
+    run_bf16_v2<128, 192, 64, 2>(X, W, M, N, K, epi, s);
+  else
+    run_bf16<128, 128>(X, W, M, N, K, epi, s);
+}
+
 // ================================================================ fp32 FMA kernel
 // 64x64 output tile, K step 16, 256 threads, 4x4 outputs per thread
 // (four consecutive columns per row, as the epilogues expect).
@@ -509,7 +683,9 @@ static void launch_typed(const Tact* X, const Tact* W, int M, int N, int K, cons
       go(EpiBiasGelu<Tact>{(const Tact*)e.bias, (Tact*)e.out, N});
       break;
     case EPI_BIAS_RESID:
-      if (e.resid_f32 && e.out_f32)
+      if (e.resid_f32 && e.out_f32 && e.resid == e.out)
+        go(EpiResidInPlace<Tact>{(const Tact*)e.bias, (float*)e.out, N});
+      else if (e.resid_f32 && e.out_f32)
         go(EpiBiasResid<Tact, float, float>{(const Tact*)e.bias, (const float*)e.resid, (float*)e.out, N});
       else if (e.resid_f32)
         go(EpiBiasResid<Tact, float, Tact>{(const Tact*)e.bias, (const float*)e.resid, (Tact*)e.out, N});
@@ -532,5 +708,7 @@ void launch_gemm(bool bf16, const void* X, const void* W, int M, int N, int K, c
   else
     launch_typed<float>((const float*)X, (const float*)W, M, N, K, e, s);
 }
+
+
 
 }  // namespace gpt2

@@ -31,12 +31,11 @@ constexpr int kMaxRowKeysF32 = 8192;  // fp32 row-wise attention keeps a row of 
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t x, a, q, o, u, kv, part, total;
+  size_t x, a, q, o, u, kv, total;
 };
 
 // Workspace regions for M = B*T rows: fp32 residual x, LN output a, q, attention
-// output o, MLP hidden u, K/V scratch (when no present/cache is given) and the
-// decode split partials.
+// output o, MLP hidden u and K/V scratch (when no present/cache is given).
 Layout layout(const gpt2_hparams& hp, gpt2_mode mode, int B, int T) {
   const size_t act = mode == GPT2_BF16 ? 2 : 4;
   const size_t M = (size_t)B * T, d = (size_t)hp.n_embd;
@@ -48,8 +47,6 @@ Layout layout(const gpt2_hparams& hp, gpt2_mode mode, int B, int T) {
   L.o = off;  off += up(M * d * act);
   L.u = off;  off += up(M * 4 * d * act);
   L.kv = off; off += up(2 * M * d * act);
-  L.part = off;
-  off += up(decode_part_floats(B, hp.n_head, hp.n_ctx) * sizeof(float));
   L.total = off;
   return L;
 }
@@ -97,11 +94,11 @@ gpt2_status hip_status() { return hipGetLastError() == hipSuccess ? GPT2_OK : GP
 // a HIP event pair on its stream; events are created once and reused.
 enum Kern {
   K_EMBED, K_LAYERNORM, K_GEMM_C_ATTN, K_GEMM_ATTN_PROJ, K_GEMM_C_FC, K_GEMM_MLP_PROJ, K_GEMM_HEAD,
-  K_ATTN_PREFILL, K_ATTN_ROWS, K_ATTN_DEC_SPLIT, K_ATTN_DEC_COMBINE, K_COUNT
+  K_ATTN_PREFILL, K_ATTN_ROWS, K_ATTN_DECODE, K_COUNT
 };
 const char* const kKernNames[K_COUNT] = {
     "embed", "layernorm", "gemm_c_attn", "gemm_attn_c_proj", "gemm_c_fc", "gemm_mlp_c_proj",
-    "gemm_lm_head", "attn_prefill", "attn_rows_f32", "attn_decode_split", "attn_decode_combine"};
+    "gemm_lm_head", "attn_prefill", "attn_rows_f32", "attn_decode"};
 
 struct Timing {
   bool on = false;
@@ -180,9 +177,7 @@ struct Run {
     if (!b16) {
       timed(K_ATTN_ROWS, s, [&] { launch_attn_rows_f32((const float*)q, kv, (float*)o, B, H, T, dh, l_past, s); });
     } else if (decode) {
-      float* part = (float*)at(L.part);
-      timed(K_ATTN_DEC_SPLIT, s, [&] { launch_attn_decode_split((const bf16_t*)q, kv, part, B, H, l_past, s); });
-      timed(K_ATTN_DEC_COMBINE, s, [&] { launch_attn_decode_combine(part, (bf16_t*)o, B, H, l_past, s); });
+      timed(K_ATTN_DECODE, s, [&] { launch_attn_decode_bf16((const bf16_t*)q, kv, (bf16_t*)o, B, H, l_past, s); });
     } else {
       timed(K_ATTN_PREFILL, s, [&] { launch_attn_prefill_bf16((const bf16_t*)q, kv, (bf16_t*)o, B, H, T, l_past, s); });
     }

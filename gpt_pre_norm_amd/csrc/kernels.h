@@ -44,7 +44,9 @@ struct Epilogue {
 };
 
 // Y = X W^T with the epilogue; X [M, K], W [N, K] row-major.
-// bf16: MFMA path (K % 8 == 0); else fp32 FMA path (K % 4 == 0).
+// bf16: MFMA paths (K % 8 == 0; M <= 64 uses the weight-streaming skinny
+// kernel when K allows); else fp32 FMA path (K % 4 == 0).  An in-place fp32
+// residual update (resid == out) may be accumulated with fp32 atomics.
 void launch_gemm(bool bf16, const void* X, const void* W, int M, int N, int K, const Epilogue& e,
                  hipStream_t s);
 
@@ -58,11 +60,8 @@ void launch_attn_prefill_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int 
 // Row-wise reference-style kernel (fp32 mode, any T, d_h % 4 == 0, d_h <= 128).
 void launch_attn_rows_f32(const float* q, KvView kv, float* o, int B, int H, int T, int d_head,
                           int l_past, hipStream_t s);
-// Single-token decode (bf16, d_h == 64): split over keys + combine.
-// part: workspace of decode_part_floats(B, H, l_past) floats.
-size_t decode_part_floats(int B, int H, int n_keys);
-void launch_attn_decode_split(const bf16_t* q, KvView kv, float* part, int B, int H, int l_past,
-                              hipStream_t s);
-void launch_attn_decode_combine(const float* part, bf16_t* o, int B, int H, int l_past, hipStream_t s);
+// Single-token decode (bf16, d_h == 64): one workgroup per (sequence, head).
+void launch_attn_decode_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int l_past,
+                             hipStream_t s);
 
 }  // namespace gpt2

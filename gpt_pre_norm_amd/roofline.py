@@ -13,7 +13,7 @@ RIDGE = PEAK_BF16_FLOPS / PEAK_HBM_BYTES
 
 
 def kernel_work(kind: str, *, B: int, T: int, d: int, h: int, V: int, l_past: int = 0,
-                act: int = 2, decode_split_keys: int = 256) -> tuple[float, float]:
+                act: int = 2) -> tuple[float, float]:
     """(flops, bytes) of one launch of a kernel kind in the bf16 path."""
     M = B * T
     dh = d // h
@@ -42,16 +42,11 @@ def kernel_work(kind: str, *, B: int, T: int, d: int, h: int, V: int, l_past: in
         flops = 4.0 * pairs * dh
         byt = 4.0 * M * d * act  # q, k, v read once, o written once
         return flops, byt
-    if kind == "attn_decode_split":
+    if kind == "attn_decode":
         nk = l_past + 1
-        ns = -(-nk // decode_split_keys)
         flops = 4.0 * B * h * nk * dh
-        byt = 2.0 * B * h * nk * dh * act + B * d * act + B * h * ns * (dh + 2) * 4
+        byt = 2.0 * B * h * nk * dh * act + 2 * B * d * act  # K and V rows, q in, o out
         return flops, byt
-    if kind == "attn_decode_combine":
-        nk = l_past + 1
-        ns = -(-nk // decode_split_keys)
-        return 0.0, B * h * ns * (dh + 2) * 4 + B * d * act
     raise KeyError(kind)
 
 

@@ -136,7 +136,7 @@ gpt2_status gpt2_read_device_flags(void *ws, void *stream);
  * are host-side objects the library creates once and reuses (no device
  * memory).  gpt2_timing_end() waits for the last event, sums the elapsed time
  * per kernel kind, writes at most max_entries records to `out` (name: static
- * string such as "gemm_c_fc" or "attn_decode_split") and returns the number
+ * string such as "gemm_c_fc" or "attn_decode") and returns the number
  * of kinds seen, or -1 if timing was not on or a HIP call failed.  Not
  * thread-safe: one timing session per process at a time. */
 typedef struct {

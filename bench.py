@@ -19,7 +19,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps K2]
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -46,28 +45,23 @@ def parse():
     return ap.parse_args()
 
 
-def traffic_for(kernel: str):
-    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE counters,
-    committed in profiles/traffic.json together with a hash of the kernel sources;
-    None when absent or when the sources changed since the counters were taken."""
+def traffic_for(phase: str, kernel: str):
+    """HBM-side bytes per launch of a kernel kind, measured with rocprofv3
+    FETCH_SIZE / WRITE_SIZE counters (scaled by a calibration copy) and kept in
+    profiles/traffic.json with a hash of the kernel sources; None when absent or
+    when the sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(kernel)
-    except (OSError, ValueError):
+        from gpt_pre_norm_amd.profiling import sources_sha
+        rec = json.load(open(path))
+    except (OSError, ValueError, ImportError):
         return None
-    if not rec or rec.get("source_sha") != sources_sha():
+    if rec.get("source_sha") != sources_sha():
         return None
-    return rec.get("bytes_per_launch")
-
-
-def sources_sha() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "gpt_pre_norm_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
+    k = rec.get(phase, {}).get(kernel)
+    return None if k is None else round(k["bytes_per_launch"])
 
 
 def main():
@@ -152,7 +146,7 @@ def main():
     else:
         achieved, peak, unit = b / avg_s / 1e9, R.PEAK_HBM_BYTES / 1e9, "GB/s"
     roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": traffic_for(dom),
+                "frac": round(achieved / peak, 4), "traffic": traffic_for("forward", dom),
                 "work_per_launch": f if bound == "mfma" else b, "avg_launch_us": round(avg_s * 1e6, 2)}
 
     result = {
@@ -261,7 +255,7 @@ def bench_decode(args, G, R, synth, wl, Wd, hp, stream, dev):
         "algorithmic_bytes_per_step": byt,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": R.PEAK_HBM_BYTES / 1e9,
                      "unit": "GB/s", "frac": round(ach * 1e9 / R.PEAK_HBM_BYTES, 4),
-                     "traffic": traffic_for(dom), "work_per_launch": b, "avg_launch_us": round(avg_s * 1e6, 2)},
+                     "traffic": traffic_for("decode", dom), "work_per_launch": b, "avg_launch_us": round(avg_s * 1e6, 2)},
         "kernels": kernels,
     }
 

@@ -7,8 +7,8 @@
 //
 // Three kernels:
 //  * attn_prefill_bf16: flash-style, 128 queries per workgroup (32 per wave),
-//    64-key K/V tiles staged through LDS (double buffered), online softmax in
-//    fp32 with exp2, MFMA 32x32x16 bf16 for Q K^T and P V.  Key tiles past the
+//    64-key K and V^T tiles moved to LDS by DMA through a 4-deep ring, online
+//    softmax in fp32 with exp2, MFMA 32x32x16 bf16 for Q K^T and P V.  Key tiles past the
 //    causal frontier are never loaded; tiles entirely above a wave's queries
 //    are skipped by that wave; only diagonal tiles apply the mask.
 //  * attn_rows_f32: one wave per query row with a full (max-subtracted)
@@ -26,22 +26,41 @@ static constexpr float kLog2e = 1.4426950408889634f;
 // MFMA v_mfma_f32_32x32x16_bf16 throughout.  A wave owns 32 queries; per 64-key
 // tile it computes S^T = K Q^T (keys on the MFMA rows, queries on the columns,
 // so each lane holds 32 scores of one query), runs the online softmax in fp32
-// with exp2, and accumulates O^T += V^T P^T.  The P fragment is the S fragment
-// converted to bf16 in place: within a 16-key MFMA step, lane half kh supplies
-// keys {4kh..4kh+3, 8+4kh..8+4kh+3}, and the V^T operand is read with the same
-// key order, so P never leaves registers.
+// with exp2, and accumulates O^T += V^T P^T.
 //
-// LDS: K tile [64 keys][64 d] with 16-byte chunks XOR-swizzled by (row>>1)&7;
-// V^T tile [64 d][64 keys] with 8-byte key quads XOR-swizzled by (d>>1)&15.
-// Both swizzles make the fragment reads conflict-free.  Double buffered.
-GPT2_DEV int vt_swz(int d) { return (d >> 1) & 15; }
+// Key order: the S MFMA reads K row pi(i) for its row i, pi swapping bits 2 and
+// 3 of i.  A lane's score registers r = 0..15 then hold keys 16*(r/8) + 8*kh +
+// r%8 of the 32-key block, so the bf16 P fragment of each 16-key P*V step is
+// 8 consecutive keys per lane half: the matching V^T operand is one 16-byte
+// chunk of a V^T row, and P never leaves registers.
+//
+// K and V tiles [64 keys][64 d] are copied from the cache rows global -> LDS
+// with global_load_lds_dwordx4 through a ring of STAGES buffers, STAGES-1 tiles
+// ahead.  The V^T operand is read with the gfx950 transposing LDS read
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane 4k+q supplies the address
+// of dims 4q..4q+3 of key k and lane i receives key 0..3 of dim i, so two such
+// reads give a lane its 8 consecutive keys of one dim.  16-byte chunks are
+// XOR-swizzled per row: K by (key>>1)&7 (conflict-free 16-row fragment reads),
+// V by 4*((key>>1)&1) (conflict-free 4-row x 32-dim transposing reads).
+constexpr int kAttnStages = 4;
+constexpr int kAttnStageU4 = 2 * 64 * 8;  // K tile + V^T tile, uint4 units
+
+GPT2_DEV int key_perm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+template <int N>
+GPT2_DEV void attn_wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+
+GPT2_DEV int v_swz(int key) { return ((key >> 1) & 1) << 2; }
 
 __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __restrict__ q,
                                                                 KvView kv, bf16_t* __restrict__ o,
-                                                                int H, int T, int l_past, int nqb) {
+                                                                int H, int T, int nqb) {
   constexpr int D = 64;
-  __shared__ uint4 ks[2][64 * 8];      // K tile, 16-byte chunks
-  __shared__ uint2 vt[2][64 * 16];     // V^T tile, 8-byte key quads
+  __shared__ uint4 lds[kAttnStages * kAttnStageU4];  // 64 KB
 
   const int qb = nqb - 1 - (int)blockIdx.y;  // longest rows first
   const int bh = blockIdx.x;
@@ -50,11 +69,11 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
   const int l32 = lane & 31, kh = lane >> 5;
 
   const int q0 = qb * 128;
-  const int qw0 = q0 + wave * 32;                       // this wave's first query (relative)
-  const int kend = l_past + min(q0 + 128, T);           // keys needed by the workgroup
+  const int qw0 = q0 + wave * 32;          // this wave's first query
+  const int kend = min(q0 + 128, T);       // keys needed by the workgroup
   const int nkb = (kend + 63) / 64;
-  const int wave_last = l_past + min(qw0 + 31, T - 1);  // last position this wave needs
-  const int qpos = l_past + qw0 + l32;                  // this lane's query position
+  const int wave_last = min(qw0 + 31, T - 1);
+  const int qpos = qw0 + l32;              // this lane's query position
 
   const bf16_t* kbase = (const bf16_t*)kv.base + b * kv.sb + h * kv.sh;
   const bf16_t* vbase = kbase + kv.skv;
@@ -70,37 +89,33 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
           bf16x8_t, *reinterpret_cast<const uint4*>(qbase + (long long)t * D + 16 * ds + 8 * kh));
   }
 
-  // loader mapping: K rows tid>>3 (+32), chunk tid&7; V key pair tid>>3, dims 8*(tid&7)
-  const int lr = tid >> 3, lc = tid & 7;
-  uint4 rk[2], rv[2];
-  auto gload = [&](int kb) {
+  // loads: this wave fills K and V rows 8*wave.. and 8*(wave+4)..
+  const int lrow = lane >> 3, lpc = lane & 7;
+  auto issue = [&](int kb, int st) {
     const int key0 = kb * 64;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int key = min(key0 + lr + 32 * i, kend - 1);
-      rk[i] = *reinterpret_cast<const uint4*>(kbase + (long long)key * D + lc * 8);
-      const int vkey = min(key0 + 2 * lr + i, kend - 1);
-      rv[i] = *reinterpret_cast<const uint4*>(vbase + (long long)vkey * D + lc * 8);
+      const int g = wave + 4 * i;
+      const int row = 8 * g + lrow;
+      const int key = min(key0 + row, kend - 1);
+      const int ck = lpc ^ ((row >> 1) & 7);
+      const int cv = lpc ^ v_swz(row);
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + (long long)key * D + ck * 8),
+                                       (__attribute__((address_space(3))) void*)(lds + st * kAttnStageU4 + g * 64),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + (long long)key * D + cv * 8),
+                                       (__attribute__((address_space(3))) void*)(lds + st * kAttnStageU4 + 512 + g * 64),
+                                       16, 0, 0);
     }
   };
-  auto lstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = lr + 32 * i;
-      ks[st][r * 8 + (lc ^ ((r >> 1) & 7))] = rk[i];
-    }
-    // transpose keys (2*lr, 2*lr+1) x dims 8*lc..8*lc+7 into V^T
-    const uint32_t a[4] = {rv[0].x, rv[0].y, rv[0].z, rv[0].w};
-    const uint32_t c[4] = {rv[1].x, rv[1].y, rv[1].z, rv[1].w};
-    const int kq = lr >> 1, half = lr & 1;
-    uint32_t* vt32 = reinterpret_cast<uint32_t*>(vt[st]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = lc * 8 + e;
-      const uint32_t lo = (e & 1) ? (a[e >> 1] >> 16) : (a[e >> 1] & 0xFFFFu);
-      const uint32_t hi = (e & 1) ? (c[e >> 1] >> 16) : (c[e >> 1] & 0xFFFFu);
-      vt32[(d * 16 + (kq ^ vt_swz(d))) * 2 + half] = lo | (hi << 16);
-    }
+  // transposing-read addresses (bytes within a V tile): lane group G = lane/16
+  // holds dims 16*(G&1) (+32*db) and keys 8*(G>>1) (+16*ksx, +4 for the second read)
+  const int tq = (lane & 15) & 3, tk = (lane & 15) >> 2;
+  const int tdim0 = 16 * ((lane >> 4) & 1) + 4 * tq;  // + 32*db
+  const int tkey0 = 8 * (lane >> 5) + tk;             // + 16*ksx (+4)
+  auto tr_addr = [&](int key, int dim) {  // byte offset of (key, dims dim..dim+3)
+    const int c = dim >> 3;
+    return key * 128 + ((c ^ v_swz(key)) << 4) + ((dim & 4) << 1);
   };
 
   f32x16_t oacc[2];
@@ -111,13 +126,19 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
   float mrun = -INFINITY, lrun = 0.f;
   const float sc = 0.125f * kLog2e;  // 1/sqrt(64), in the log2 domain
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < kAttnStages - 1; ++s)
+    if (s < nkb) issue(s, s);
+
   for (int kb = 0; kb < nkb; ++kb) {
-    const bool more = kb + 1 < nkb;
-    if (more) gload(kb + 1);
-    const int st = kb & 1;
+    const int ahead = min(kAttnStages - 2, nkb - 1 - kb);
+    if (ahead >= 2) attn_wait_vmcnt<8>();
+    else if (ahead == 1) attn_wait_vmcnt<4>();
+    else attn_wait_vmcnt<0>();
+    __syncthreads();
+    if (kb + kAttnStages - 1 < nkb) issue(kb + kAttnStages - 1, (kb + kAttnStages - 1) % kAttnStages);
+    const uint4* ks = lds + (kb % kAttnStages) * kAttnStageU4;
+    const uint4* vs = ks + 512;
     const int key0 = kb * 64;
     if (key0 <= wave_last) {
       // ---- S^T for 2 x 32 keys
@@ -126,39 +147,50 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
       for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kk][r] = 0.f;
-        const int row = kk * 32 + l32;
+        const int row = kk * 32 + key_perm(l32);
 #pragma unroll
         for (int ds = 0; ds < 4; ++ds) {
           const int chunk = 2 * ds + kh;
-          const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, ks[st][row * 8 + (chunk ^ ((row >> 1) & 7))]);
+          const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, ks[row * 8 + (chunk ^ ((row >> 1) & 7))]);
           s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kk], 0, 0, 0);
         }
       }
-      // ---- mask (diagonal tiles only) and online softmax; lane's keys:
-      // key0 + 32*kk + 8*(r/4) + 4*kh + r%4
-      const bool need_mask = key0 + 63 > l_past + qw0;
+      // ---- mask (diagonal tiles only) and online softmax; register r of block
+      // kk holds key key0 + 32*kk + 16*(r/8) + 8*kh + r%8.  The reference max
+      // mref only moves when the tile max exceeds it by more than 8 (log2
+      // units): weights are then at most 2^8, exact in fp32 and in bf16's range,
+      // and the O / sum rescale is skipped for most tiles.  Both use the same
+      // mref, so the final O / sum is the softmax.
+      if (key0 + 63 > qw0) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (key0 + 32 * kk + 16 * (r >> 3) + 8 * kh + (r & 7) > qpos) s[kk][r] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = s[kk][r] * sc;
-          if (need_mask && key0 + 32 * kk + 8 * (r >> 2) + 4 * kh + (r & 3) > qpos) v = -INFINITY;
-          s[kk][r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrun, mx);
-      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-      mrun = mnew;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kk][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sc;
+      if (mx > mrun + 8.0f) {
+        const float alpha = __builtin_amdgcn_exp2f(mrun - mx);  // 0 on the first tile
+        mrun = mx;
+        lrun *= alpha;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+      }
       float ls = 0.f;
-      bf16x8_t pf[4];  // 16-key MFMA steps
+      bf16x8_t pf[4];  // 16-key P*V steps
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(s[kk][r] - mnew);
+          p[r] = __builtin_amdgcn_exp2f(fmaf(s[kk][r], sc, -mrun));
           ls += p[r];
         }
 #pragma unroll
@@ -169,32 +201,30 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
                                    pack_bf2(pp[6], pp[7])));
         }
       }
-      lrun = lrun * alpha + ls;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-      // ---- O^T += V^T P^T over 4 steps of 16 keys
+      lrun += ls;
+      // ---- O^T += V^T P^T over 4 steps of 16 keys (transposing reads of V)
+      const char* vbytes = reinterpret_cast<const char*>(vs);
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        const int d = db * 32 + l32;
-        const uint2* vrow = &vt[st][d * 16];
 #pragma unroll
         for (int ksx = 0; ksx < 4; ++ksx) {
-          const uint2 x1 = vrow[(4 * ksx + kh) ^ vt_swz(d)];
-          const uint2 x2 = vrow[(4 * ksx + 2 + kh) ^ vt_swz(d)];
-          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(x1.x, x1.y, x2.x, x2.y));
+          const int key = 16 * ksx + tkey0;
+          const int dim = 32 * db + tdim0;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(vbytes + tr_addr(key, dim)));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(vbytes + tr_addr(key + 4, dim)));
+          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ksx], oacc[db], 0, 0, 0);
         }
       }
     }
-    if (more) lstore((kb + 1) & 1);
-    __syncthreads();
   }
 
   // ---- normalise and store O [B, T, H*64]; lane holds query qw0 + l32 and
   // dims 32*db + 8*(r/4) + 4*kh + r%4
-  float l = lrun + __shfl_xor(lrun, 32, 64);
+  const float l = lrun + __shfl_xor(lrun, 32, 64);
   const float inv = 1.0f / l;
   const int t = qw0 + l32;
   if (t < T) {
@@ -210,11 +240,10 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
   }
 }
 
-void launch_attn_prefill_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int T, int l_past,
-                              hipStream_t s) {
+void launch_attn_prefill_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int T, hipStream_t s) {
   const int nqb = (T + 127) / 128;
   dim3 grid(B * H, nqb);
-  attn_prefill_bf16_kernel<<<grid, 256, 0, s>>>(q, kv, o, H, T, l_past, nqb);
+  attn_prefill_bf16_kernel<<<grid, 256, 0, s>>>(q, kv, o, H, T, nqb);
 }
 
 // ================================================================ row-wise (fp32)

@@ -15,13 +15,17 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 GPT2_DEV float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// fp32 -> bf16, round to nearest even (inputs are finite).
-GPT2_DEV bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (bf16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+
+// Two fp32 -> packed bf16 (a in the low half), round to nearest even, with the
+// gfx950 conversion instruction v_cvt_pk_bf16_f32.
+GPT2_DEV uint32_t pack_bf2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-GPT2_DEV uint32_t pack_bf2(float a, float b) { return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16); }
+// fp32 -> bf16, round to nearest even.
+GPT2_DEV bf16_t f2bf(float f) { return (bf16_t)(pack_bf2(f, 0.f) & 0xFFFFu); }
 
 // Low/high bf16 of a packed pair, as fp32.
 GPT2_DEV float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }

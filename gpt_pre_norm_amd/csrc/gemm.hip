@@ -440,8 +440,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_v2_kernel(const bf16_t* __restr
 }
 
 template <int BM, int BN, int BK, int STAGES, class Epi>
-static void run_bf16_v2(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
+static void run_bf16_v2(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi_in,
                         hipStream_t s) {
+  const Epi& epi = epi_in;
   using C = V2Cfg<BM, BN, BK, STAGES>;
   static bool attr_set = false;  // one-time, per template instance
   if (!attr_set) {

@@ -172,6 +172,7 @@ struct Run {
     e.n_head = H;
     e.d_head = dh;
     e.d = d;
+
     timed(K_GEMM_C_ATTN, s, [&] { launch_gemm(b16, a, w.attn_w, m, 3 * d, d, e, s); });
     // causal attention -> o [B, T, d]
     if (!b16) {
@@ -179,7 +180,7 @@ struct Run {
     } else if (decode) {
       timed(K_ATTN_DECODE, s, [&] { launch_attn_decode_bf16((const bf16_t*)q, kv, (bf16_t*)o, B, H, l_past, s); });
     } else {
-      timed(K_ATTN_PREFILL, s, [&] { launch_attn_prefill_bf16((const bf16_t*)q, kv, (bf16_t*)o, B, H, T, l_past, s); });
+      timed(K_ATTN_PREFILL, s, [&] { launch_attn_prefill_bf16((const bf16_t*)q, kv, (bf16_t*)o, B, H, T, s); });
     }
     // c_proj + bias + residual -> x1 (fp32)
     Epilogue p{};

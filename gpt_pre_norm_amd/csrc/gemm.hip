@@ -260,18 +260,18 @@ static void run_bf16(const bf16_t* X, const bf16_t* W, int M, int N, int K, cons
 // the global 16-byte chunk that the XOR swizzle puts in its slot, so the
 // fragment reads (16 lanes = 16 rows of one chunk) touch all 64 banks once.
 // Requires K % BK == 0.
-template <int BM, int BN, int BK, int STAGES>
+template <int BM, int BN, int BK, int STAGES, int NW = 4>
 struct V2Cfg {
   static constexpr int CH = BK / 8;                  // 16-byte chunks per row
   static constexpr int RPL = 64 / CH;                // rows per wave load (1 KB)
   static constexpr int SWZ_SHIFT = BK == 64 ? 1 : 2; // rows sharing a bank phase
   static constexpr int ROWS = BM + BN;               // X rows then W rows
   static constexpr int GROUPS = ROWS / RPL;          // wave loads per stage
-  static constexpr int LOADS = GROUPS / 4;           // per wave per stage
+  static constexpr int LOADS = GROUPS / NW;          // per wave per stage
   static constexpr int STAGE_U4 = ROWS * CH;         // uint4 per stage
   static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_U4 * 16;
   static_assert(BK == 32 || BK == 64, "BK");
-  static_assert(GROUPS % 4 == 0, "row groups must split evenly over 4 waves");
+  static_assert(GROUPS % NW == 0, "row groups must split evenly over the waves");
   static_assert(BM % 64 == 0 && BN % 64 == 0, "wave tiles are multiples of 32");
   static GPT2_DEV int swz(int row, int c) { return c ^ ((row >> SWZ_SHIFT) & (CH - 1)); }
 };
@@ -304,12 +304,14 @@ GPT2_DEV void wait_stage(int ahead) {
   wait_vmcnt<0>();
 }
 
-template <int BM, int BN, int BK, int STAGES, class Epi>
-__global__ __launch_bounds__(256) void gemm_bf16_v2_kernel(const bf16_t* __restrict__ X,
-                                                           const bf16_t* __restrict__ W, int M, int N,
-                                                           int K, Epi epi, int tiles_m, int tiles_n) {
-  using C = V2Cfg<BM, BN, BK, STAGES>;
-  constexpr int WM = BM / 2, WN = BN / 2;
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, class Epi>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_v2_kernel(const bf16_t* __restrict__ X,
+                                                                      const bf16_t* __restrict__ W, int M,
+                                                                      int N, int K, Epi epi, int tiles_m,
+                                                                      int tiles_n) {
+  constexpr int NW = WGM * WGN;
+  using C = V2Cfg<BM, BN, BK, STAGES, NW>;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int KS = BK / 16;  // MFMA steps per stage
   extern __shared__ uint4 lds[];
@@ -318,13 +320,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_v2_kernel(const bf16_t* __restr
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm_idx, tn_idx);
   const int m0 = tm_idx * BM, n0 = tn_idx * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WGM, wn = wave / WGM;
 
   // this lane's source row / chunk for each of its wave's row groups
   const bf16_t* src[C::LOADS];
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
-    const int g = wave + 4 * i;
+    const int g = wave + NW * i;
     const int row = C::RPL * g + lane / C::CH;
     const int c = C::swz(row, lane % C::CH);
     const bf16_t* base = row < BM ? X + (long long)min(m0 + row, M - 1) * K
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_v2_kernel(const bf16_t* __restr
     const int k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int g = wave + 4 * i;
+      const int g = wave + NW * i;
       uint4* dst = lds + stage * C::STAGE_U4 + g * 64;
       __builtin_amdgcn_global_load_lds((const void*)(src[i] + k0),
                                        (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
@@ -439,20 +441,19 @@ __global__ __launch_bounds__(256) void gemm_bf16_v2_kernel(const bf16_t* __restr
   }
 }
 
-template <int BM, int BN, int BK, int STAGES, class Epi>
-static void run_bf16_v2(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi_in,
+template <int BM, int BN, int BK, int STAGES, class Epi, int WGM = 2, int WGN = 2>
+static void run_bf16_v2(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
                         hipStream_t s) {
-  const Epi& epi = epi_in;
-  using C = V2Cfg<BM, BN, BK, STAGES>;
+  using C = V2Cfg<BM, BN, BK, STAGES, WGM * WGN>;
   static bool attr_set = false;  // one-time, per template instance
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)gemm_bf16_v2_kernel<BM, BN, BK, STAGES, Epi>,
+    (void)hipFuncSetAttribute((const void*)gemm_bf16_v2_kernel<BM, BN, BK, STAGES, WGM, WGN, Epi>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
     attr_set = true;
   }
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  gemm_bf16_v2_kernel<BM, BN, BK, STAGES, Epi><<<tiles_m * tiles_n, 256, C::LDS_BYTES, s>>>(
-      X, W, M, N, K, epi, tiles_m, tiles_n);
+  gemm_bf16_v2_kernel<BM, BN, BK, STAGES, WGM, WGN, Epi>
+      <<<tiles_m * tiles_n, 64 * WGM * WGN, C::LDS_BYTES, s>>>(X, W, M, N, K, epi, tiles_m, tiles_n);
 }
 
 // ================================================================ skinny bf16 kernel (M <= 64)
@@ -607,7 +608,7 @@ static void dispatch_bf16(const bf16_t* X, const bf16_t* W, int M, int N, int K,
   if (M <= 64)
     run_bf16<64, 64>(X, W, M, N, K, epi, s);
   else if (K % 64 == 0)
-    run_bf16_v2<128, 192, 64, 2>(X, W, M, N, K, epi, s);
+    run_bf16_v2<128, 192, 64, 2, Epi, 4, 2>(X, W, M, N, K, epi, s);
   else
     run_bf16<128, 128>(X, W, M, N, K, epi, s);
 }

@@ -10,8 +10,12 @@ typedef uint16_t bf16_t;  // bfloat16 storage (bit pattern)
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+// f32x4 at 4-byte alignment (gfx9 vector memory accepts dword-aligned dwordx4)
+typedef __attribute__((__vector_size__(4 * sizeof(float)), __aligned__(4))) float f32x4u_t;
 
 #define GPT2_DEV __device__ __forceinline__
+// for lambdas whose reference-captured register arrays must not go to memory
+#define GPT2_INLINE __attribute__((always_inline))
 
 GPT2_DEV float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
 

@@ -3,16 +3,21 @@
 // (+bias +residual), c_fc (+bias, GELU) and the tied head (wte^T, fp32 logits).
 // ("Decoder Block", How it works; "Full Forward Pass", How it works.)
 //
-// bf16 path: MFMA v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Both
-// operands are K-contiguous ([rows, K] row-major), which is the layout the MFMA
-// fragments want.  The W tile is the MFMA A operand and the X tile the B
-// operand, so each lane's four accumulators are four consecutive output
-// columns of one row: the epilogue does 8/16-byte vector stores.
-// Tiles are staged through LDS with a double buffer (one barrier per K step)
-// and an XOR swizzle of the 16-byte chunks so fragment reads are conflict-free.
-//
+// Both operands are K-contiguous ([rows, K] row-major), the layout the MFMA
+// fragments want; the W tile is the MFMA A operand and the X tile the B
+// operand, so each lane's accumulators hold consecutive output columns of one
+// row.  bf16 kernels, by shape:
+//   * M > 64, K % 64 == 0: 128x192 tiles (the head: 256x256), 8 waves of
+//     v_mfma_f32_32x32x16_bf16, tiles DMA'd global -> LDS with
+//     global_load_lds_dwordx4 through a two-stage ring, epilogue through a
+//     per-wave LDS patch so stores cover whole rows of 128 bytes;
+//   * M <= 64 (decode): a weight-streaming kernel with split K;
+//   * otherwise: a register-staged 16x16x32 kernel.
 // fp32 path: a plain LDS-tiled FMA kernel (correctness mode).
 #include "kernels.h"
+
+#include <type_traits>
+#include <utility>
 
 namespace gpt2 {
 
@@ -24,15 +29,67 @@ struct EpiStoreF32 {
   static constexpr bool kRowStore = true;
   float* out;
   int N;
+  struct Ctx {};
+  GPT2_DEV Ctx load(int, int) const { return {}; }
+  GPT2_DEV void store(int m, int n, f32x4_t v, Ctx) const { (*this)(m, n, v); }
   GPT2_DEV void store1(int m, int n, float v) const { out[(long long)m * N + n] = v; }
   GPT2_DEV void operator()(int m, int n, f32x4_t v) const {
     float* p = out + (long long)m * N + n;
     if (n + 3 < N) {
-      p[0] = v[0]; p[1] = v[1]; p[2] = v[2]; p[3] = v[3];
+      *reinterpret_cast<f32x4u_t*>(p) = v;  // one dwordx4 store, 4-byte aligned
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (n + r < N) p[r] = v[r];
+    }
+  }
+};
+
+// The head's fp32 logits through the 128x192 MFMA kernel, written in whole
+// 128-byte lines.  Rows of [M, N] start at arbitrary 4-byte phases (N is odd),
+// so plain column tiles share a partial line with their neighbours in every
+// row, and partial-line writes run at well under half the write bandwidth.
+// Instead the kernel's tile rows are positions in an order that groups rows by
+// phase (row m = r + 32 j, r = class, in class-major order), all rows of a
+// tile share one phase, and the tile's column window starts on a line boundary
+// of those rows (window origin = that phase's offset + BN * (tn - 1), so one
+// extra window per row block covers the leading columns).  Results are the
+// same; only which tile writes which element changes.
+struct EpiStoreF32Lines {
+  float* out;
+  int N, M;
+  int q, s;  // M = 32 q + s: classes r < s hold q + 1 rows, the others q
+  static EpiStoreF32Lines make(float* out, int N, int M) { return {out, N, M, M >> 5, M & 31}; }
+  // row of position i in the class-major order
+  GPT2_DEV int row_of(int i) const {
+    const int big = s * (q + 1);
+    int r, j;
+    if (i < big) {
+      r = i / (q + 1);
+      j = i - r * (q + 1);
+    } else {
+      const int i2 = i - big;
+      r = s + i2 / q;
+      j = i2 - (r - s) * q;
+    }
+    return r + 32 * j;
+  }
+  // columns from the start of row_of(i) to its first 128-byte line boundary
+  GPT2_DEV int line_offset(int i) const {
+    const long long w = (long long)((uintptr_t)out >> 2) + (long long)row_of(i) * N;
+    return (int)(-w & 31);
+  }
+  struct Ctx {};
+  GPT2_DEV Ctx load(int, int) const { return {}; }
+  GPT2_DEV void store(int i, int n, f32x4_t v, Ctx) const { (*this)(i, n, v); }
+  GPT2_DEV void operator()(int i, int n, f32x4_t v) const {
+    float* p = out + (long long)row_of(i) * N + n;
+    if (n >= 0 && n + 3 < N) {
+      *reinterpret_cast<f32x4u_t*>(p) = v;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r >= 0 && n + r < N) p[r] = v[r];
     }
   }
 };
@@ -42,12 +99,14 @@ struct EpiBiasGelu {
   const Tact* bias;
   Tact* out;
   int N;
-  GPT2_DEV void operator()(int m, int n, f32x4_t v) const {
-    const float4 b = load4(bias + n);
+  using Ctx = float4;  // bias
+  GPT2_DEV Ctx load(int, int n) const { return load4(bias + n); }
+  GPT2_DEV void store(int m, int n, f32x4_t v, const Ctx& b) const {
     store4(out + (long long)m * N + n,
            make_float4(gelu_tanh(v[0] + b.x), gelu_tanh(v[1] + b.y), gelu_tanh(v[2] + b.z),
                        gelu_tanh(v[3] + b.w)));
   }
+  GPT2_DEV void operator()(int m, int n, f32x4_t v) const { store(m, n, v, load(m, n)); }
 };
 
 template <typename Tact, typename Tres, typename Tout>
@@ -56,13 +115,16 @@ struct EpiBiasResid {
   const Tres* res;
   Tout* out;
   int N;
-  GPT2_DEV void operator()(int m, int n, f32x4_t v) const {
-    const float4 b = load4(bias + n);
-    const long long o = (long long)m * N + n;
-    const float4 r = load4(res + o);
-    store4(out + o, make_float4(r.x + (v[0] + b.x), r.y + (v[1] + b.y), r.z + (v[2] + b.z),
-                                r.w + (v[3] + b.w)));
+  struct Ctx {
+    float4 b, r;  // bias, residual
+  };
+  GPT2_DEV Ctx load(int m, int n) const { return {load4(bias + n), load4(res + (long long)m * N + n)}; }
+  GPT2_DEV void store(int m, int n, f32x4_t v, const Ctx& c) const {
+    store4(out + (long long)m * N + n,
+           make_float4(c.r.x + (v[0] + c.b.x), c.r.y + (v[1] + c.b.y), c.r.z + (v[2] + c.b.z),
+                       c.r.w + (v[3] + c.b.w)));
   }
+  GPT2_DEV void operator()(int m, int n, f32x4_t v) const { store(m, n, v, load(m, n)); }
 };
 
 // In-place fp32 residual update x += acc + bias.  The skinny decode kernel may
@@ -74,13 +136,18 @@ struct EpiResidInPlace {
   const Tact* bias;
   float* x;
   int N;
-  GPT2_DEV void operator()(int m, int n, f32x4_t v) const {
-    const float4 b = load4(bias + n);
-    float* p = x + (long long)m * N + n;
-    const float4 r = *reinterpret_cast<const float4*>(p);
-    *reinterpret_cast<float4*>(p) =
-        make_float4(r.x + (v[0] + b.x), r.y + (v[1] + b.y), r.z + (v[2] + b.z), r.w + (v[3] + b.w));
+  struct Ctx {
+    float4 b, r;  // bias, residual
+  };
+  GPT2_DEV Ctx load(int m, int n) const {
+    return {load4(bias + n), *reinterpret_cast<const float4*>(x + (long long)m * N + n)};
   }
+  GPT2_DEV void store(int m, int n, f32x4_t v, const Ctx& c) const {
+    *reinterpret_cast<float4*>(x + (long long)m * N + n) =
+        make_float4(c.r.x + (v[0] + c.b.x), c.r.y + (v[1] + c.b.y), c.r.z + (v[2] + c.b.z),
+                    c.r.w + (v[3] + c.b.w));
+  }
+  GPT2_DEV void operator()(int m, int n, f32x4_t v) const { store(m, n, v, load(m, n)); }
   GPT2_DEV void add(int m, int n, f32x4_t v, bool with_bias) const {
     float* p = x + (long long)m * N + n;
     float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -99,8 +166,10 @@ struct EpiQKV {
   KvView kv;
   int T, l_past, H, dh, d;
   FastDiv divT, divDh;
-  GPT2_DEV void operator()(int m, int n, f32x4_t v) const {
-    const float4 b = load4(bias + n);
+  using Ctx = float4;  // bias
+  GPT2_DEV Ctx load(int, int n) const { return load4(bias + n); }
+  GPT2_DEV void operator()(int m, int n, f32x4_t v) const { store(m, n, v, load(m, n)); }
+  GPT2_DEV void store(int m, int n, f32x4_t v, const Ctx& b) const {
     const float4 y = make_float4(v[0] + b.x, v[1] + b.y, v[2] + b.z, v[3] + b.w);
     const int sec = (n >= d) + (n >= 2 * d);
     const int c = n - sec * d;
@@ -251,15 +320,14 @@ static void run_bf16(const bf16_t* X, const bf16_t* W, int M, int N, int K, cons
 }
 
 
-// ================================================================ bf16 MFMA kernel, deep pipeline
-// 32x32x16 MFMA (twice the throughput of 16x16x32 on gfx950), 2x2 waves of
-// (BM/2)x(BN/2), K step BK (32 or 64).  Tiles move global -> LDS with
+// ================================================================ bf16 MFMA kernel, DMA ring
+// 32x32x16 MFMA (twice the throughput of 16x16x32 on gfx950), WGM x WGN waves
+// of (BM/WGM)x(BN/WGN), K step BK (32 or 64).  Tiles move global -> LDS with
 // global_load_lds_dwordx4 (no register staging) through a ring of STAGES
-// buffers, issued STAGES-1 K steps ahead; one barrier per K step.  A wave's
-// 64-lane load fills 1 KB of LDS (1024/(2*BK) tile rows), and each lane picks
-// the global 16-byte chunk that the XOR swizzle puts in its slot, so the
-// fragment reads (16 lanes = 16 rows of one chunk) touch all 64 banks once.
-// Requires K % BK == 0.
+// buffers.  A wave's 64-lane load fills 1 KB of LDS (1024/(2*BK) tile rows),
+// and each lane picks the global 16-byte chunk that the XOR swizzle puts in
+// its slot, so the fragment reads (16 lanes = 16 rows of one chunk) touch all
+// 64 banks once.  Requires K % BK == 0.
 template <int BM, int BN, int BK, int STAGES, int NW = 4>
 struct V2Cfg {
   static constexpr int CH = BK / 8;                  // 16-byte chunks per row
@@ -267,14 +335,24 @@ struct V2Cfg {
   static constexpr int SWZ_SHIFT = BK == 64 ? 1 : 2; // rows sharing a bank phase
   static constexpr int ROWS = BM + BN;               // X rows then W rows
   static constexpr int GROUPS = ROWS / RPL;          // wave loads per stage
-  static constexpr int LOADS = GROUPS / NW;          // per wave per stage
+  static constexpr int LOADS = (GROUPS + NW - 1) / NW;  // per wave per stage
+  // When the groups do not split evenly, the waves short of LOADS issue a
+  // dummy load (one 16-byte line, all lanes) into a spare 1 KB of LDS that is
+  // never read, so every wave has the same count of loads in flight.
+  static constexpr bool DUMMY = LOADS * NW != GROUPS;
   static constexpr int STAGE_U4 = ROWS * CH;         // uint4 per stage
-  static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_U4 * 16;
+  static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_U4 * 16 + (DUMMY ? 1024 : 0);
   static_assert(BK == 32 || BK == 64, "BK");
-  static_assert(GROUPS % NW == 0, "row groups must split evenly over the waves");
+  static_assert(ROWS % RPL == 0, "tile rows fill whole wave loads");
   static_assert(BM % 64 == 0 && BN % 64 == 0, "wave tiles are multiples of 32");
+  static_assert((size_t)NW * 32 * 36 * 4 <= LDS_BYTES, "epilogue patches fit in the stage ring");
   static GPT2_DEV int swz(int row, int c) { return c ^ ((row >> SWZ_SHIFT) & (CH - 1)); }
 };
+
+template <class Epi>
+constexpr bool line_aligned() {
+  return std::is_same_v<Epi, EpiStoreF32Lines>;
+}
 
 template <class Epi>
 constexpr bool row_store() {
@@ -289,23 +367,94 @@ GPT2_DEV void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier for the LDS ring.  __syncthreads() also drains every
+// outstanding global access (vmcnt 0), which would wait for the loads of the
+// stages still being prefetched; this waits only for the wave's LDS
+// instructions.  Each wave has already waited (wait_stage) for its own loads of
+// the stage about to be read, so after the barrier that stage is complete.
+GPT2_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Waits until at most `ahead` later stages of this wave's loads are in flight.
 template <int LOADS, int MAXAHEAD>
 GPT2_DEV void wait_stage(int ahead) {
-  if constexpr (MAXAHEAD >= 3) {
-    if (ahead >= 3) { wait_vmcnt<3 * LOADS>(); return; }
+  if constexpr (MAXAHEAD > 0) {
+    if (ahead >= MAXAHEAD) {
+      wait_vmcnt<MAXAHEAD * LOADS>();
+      return;
+    }
+    wait_stage<LOADS, MAXAHEAD - 1>(ahead);
+  } else {
+    wait_vmcnt<0>();
   }
-  if constexpr (MAXAHEAD >= 2) {
-    if (ahead >= 2) { wait_vmcnt<2 * LOADS>(); return; }
-  }
-  if constexpr (MAXAHEAD >= 1) {
-    if (ahead >= 1) { wait_vmcnt<LOADS>(); return; }
-  }
-  wait_vmcnt<0>();
 }
 
+// Epilogue through LDS (the patch is wave-private and LDS executes a wave's
+// accesses in order, so no wait is needed between its write and read-back).
+// A C[n][m] fragment holds, per lane, column m = lane%32
+// and rows n = 8*(r/4) + 4*(lane/32) + r%4: stored directly that is 32 rows x 16 B
+// per instruction.  Each wave instead writes one 32x32 fragment at a time to
+// its own LDS patch as [m][n] (row pitch 36 floats) and reads it back with 8
+// lanes per row, so every epilogue access covers 8 rows x 32 consecutive columns.
+// (mw0, nw0) is the wave tile's first output row and column.
+template <int FM, int FN, class Epi>
+GPT2_DEV void tile_epilogue(const f32x16_t (&acc)[FN][FM], uint4* lds, const Epi& epi, int M, int N,
+                            int mw0, int nw0, int wave, int lane) {
+  const int r32 = lane & 31, khalf = lane >> 5;
+  float* patch = reinterpret_cast<float*>(lds) + wave * (32 * 36);
+  const int er = lane >> 3;        // row within an 8-row group
+  const int ec = (lane & 7) * 4;   // first of 4 columns
+#pragma unroll
+  for (int a = 0; a < FN; ++a) {
+#pragma unroll
+    for (int b = 0; b < FM; ++b) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(patch + r32 * 36 + 8 * q + 4 * khalf) =
+            make_float4(acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
+      if constexpr (row_store<Epi>()) {
+        const int n = nw0 + a * 32 + r32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 2 * i + khalf;
+          const float v = patch[row * 36 + r32];
+          const int m = mw0 + b * 32 + row;
+          if (m < M && n < N) epi.store1(m, n, v);
+        }
+      } else {
+        f32x4_t v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 t = *reinterpret_cast<const float4*>(patch + (8 * i + er) * 36 + ec);
+          v[i] = f32x4_t{t.x, t.y, t.z, t.w};
+        }
+        // the epilogue's own reads (bias, residual) for all four rows go out
+        // together, so their latency is paid once per fragment
+        const int n = nw0 + a * 32 + ec;
+        typename Epi::Ctx cx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = mw0 + b * 32 + 8 * i + er;
+          if (m < M && n < N) cx[i] = epi.load(m, n);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = mw0 + b * 32 + 8 * i + er;
+          if (m < M && n < N) epi.store(m, n, v[i], cx[i]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- v3 schedule
+// Same tiles, loads and fragments as above, with the barrier moved: a K step's
+// last MFMAs are issued after the barrier that publishes the next stage, so
+// the first fragment reads of stage kt+1 (and the barrier's own skew) overlap
+// them instead of leaving the matrix cores idle at every stage boundary.  The
+// ring is refilled right after that barrier: stage kt+STAGES goes into the
+// buffer that stage kt has just released.
 template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, class Epi>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_v2_kernel(const bf16_t* __restrict__ X,
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_v3_kernel(const bf16_t* __restrict__ X,
                                                                       const bf16_t* __restrict__ W, int M,
                                                                       int N, int K, Epi epi, int tiles_m,
                                                                       int tiles_n) {
@@ -314,23 +463,34 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_v2_kernel(const bf16
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int KS = BK / 16;  // MFMA steps per stage
+  static_assert(KS % 2 == 0, "fragment double buffer assumes an even step count");
   extern __shared__ uint4 lds[];
 
   int tm_idx, tn_idx;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm_idx, tn_idx);
-  const int m0 = tm_idx * BM, n0 = tn_idx * BN;
+  const int m0 = tm_idx * BM;
+  int n0 = tn_idx * BN;
+  if constexpr (line_aligned<Epi>()) {
+    n0 = epi.line_offset(m0) + BN * (tn_idx - 1);
+    if (n0 >= N || n0 + BN <= 0) return;  // whole workgroup: window outside the row
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WGM, wn = wave / WGM;
 
-  // this lane's source row / chunk for each of its wave's row groups
   const bf16_t* src[C::LOADS];
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
     const int g = wave + NW * i;
+    if (g >= C::GROUPS) {  // dummy load: one line of this tile's first X row
+      src[i] = X + (long long)m0 * K;
+      continue;
+    }
     const int row = C::RPL * g + lane / C::CH;
     const int c = C::swz(row, lane % C::CH);
-    const bf16_t* base = row < BM ? X + (long long)min(m0 + row, M - 1) * K
-                                  : W + (long long)min(n0 + row - BM, N - 1) * K;
+    int xr = min(m0 + row, M - 1);
+    if constexpr (line_aligned<Epi>()) xr = epi.row_of(xr);
+    const bf16_t* base = row < BM ? X + (long long)xr * K
+                                  : W + (long long)min(max(n0 + row - BM, 0), N - 1) * K;
     src[i] = base + c * 8;
   }
   auto issue = [&](int kt, int stage) {
@@ -338,7 +498,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_v2_kernel(const bf16
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int g = wave + NW * i;
-      uint4* dst = lds + stage * C::STAGE_U4 + g * 64;
+      uint4* dst = g < C::GROUPS ? lds + stage * C::STAGE_U4 + g * 64 : lds + STAGES * C::STAGE_U4;
       __builtin_amdgcn_global_load_lds((const void*)(src[i] + k0),
                                        (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
@@ -352,107 +512,78 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_v2_kernel(const bf16
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
+  const int r32 = lane & 31, khalf = lane >> 5;
+  bf16x8_t xf[2][FM], wf[2][FN];
+  // fragment f of K step ks: X rows for f < FM, W rows after
+  auto ldone = [&](int buf, const uint4* st, int ks, int f) {
+    const int chunk = 2 * ks + khalf;
+    if (f < FM) {
+      const int row = wm * WM + f * 32 + r32;
+      xf[buf][f] = __builtin_bit_cast(bf16x8_t, st[row * C::CH + C::swz(row, chunk)]);
+    } else {
+      const int row = BM + wn * WN + (f - FM) * 32 + r32;
+      wf[buf][f - FM] = __builtin_bit_cast(bf16x8_t, st[row * C::CH + C::swz(row, chunk)]);
+    }
+  };
+  // The MFMAs of one K step (fragments in `buf`) with the fragment reads of
+  // the next step (into the other buffer) spread between them.  Reads are
+  // issued after the MFMAs they must not delay, so every wait the compiler
+  // places before an MFMA is for reads that have had a whole step to land.
+  auto step = [&](int buf, const uint4* nst, int nks) {
+    constexpr int NM = FN * FM, NL = FM + FN;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      acc[i / FM][i % FM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][i / FM], xf[buf][i % FM],
+                                                                    acc[i / FM][i % FM], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int l = i * NL / NM; l < (i + 1) * NL / NM; ++l) ldone(buf ^ 1, nst, nks, l);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   const int nk = K / BK;
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
+  for (int s = 0; s < STAGES; ++s)
     if (s < nk) issue(s, s);
+  wait_stage<C::LOADS, STAGES - 1>(min(STAGES - 1, nk - 1));
+  lds_barrier();
+#pragma unroll
+  for (int f = 0; f < FM + FN; ++f) ldone(0, lds, 0, f);
 
-  const int r32 = lane & 31, khalf = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
-    // wait for this wave's loads of tile kt; later tiles stay in flight
-    wait_stage<C::LOADS, STAGES - 2>(min(STAGES - 2, nk - 1 - kt));
-    __syncthreads();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
     const uint4* st = lds + (kt % STAGES) * C::STAGE_U4;
-    // Fragments are double-buffered in registers: the LDS reads of step ks+1
-    // are issued before the MFMAs of step ks, and scheduling barriers keep the
-    // compiler from sinking them next to their uses.
-    bf16x8_t xf[2][FM], wf[2][FN];
-    auto ldfrag = [&](int buf, int ks) {
-      const int chunk = 2 * ks + khalf;
 #pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        const int row = wm * WM + f * 32 + r32;
-        xf[buf][f] = __builtin_bit_cast(bf16x8_t, st[row * C::CH + C::swz(row, chunk)]);
-      }
-#pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        const int row = BM + wn * WN + f * 32 + r32;
-        wf[buf][f] = __builtin_bit_cast(bf16x8_t, st[row * C::CH + C::swz(row, chunk)]);
-      }
-    };
-    ldfrag(0, 0);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS) ldfrag((ks + 1) & 1, ks + 1);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int a = 0; a < FN; ++a)
-#pragma unroll
-        for (int b = 0; b < FM; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][a], xf[ks & 1][b], acc[a][b], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int ks = 0; ks < KS - 1; ++ks) step(ks & 1, st, ks + 1);
+    if (kt + 1 < nk) {
+      // own loads of stage kt+1 done (later stages may stay in flight), this
+      // wave's reads of stage kt done; after the barrier both hold for all waves
+      wait_stage<C::LOADS, STAGES - 2>(min(STAGES - 2, nk - 2 - kt));
+      lds_barrier();
+      if (kt + STAGES < nk) issue(kt + STAGES, kt % STAGES);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // last step; on the final K step the reads of the following stage fetch
+    // unused data from the ring (in bounds, never consumed)
+    step(1, lds + ((kt + 1) % STAGES) * C::STAGE_U4, 0);
   }
 
-  // Epilogue through LDS (the patch is wave-private and LDS executes a wave's
-  // accesses in order, so no wait is needed between its write and read-back).
-  // A C[n][m] fragment holds, per lane, column m = r32
-  // and rows n = 8*(r/4) + 4*khalf + r%4: stored directly that is 32 rows x 16 B
-  // per instruction.  Each wave instead writes one 32x32 fragment at a time to
-  // its own LDS patch as [m][n] (row pitch 36 floats) and reads it back with 8
-  // lanes per row, so every epilogue access covers 8 rows x 32 consecutive columns.
   __syncthreads();  // all waves are done reading the K stages
-  float* patch = reinterpret_cast<float*>(lds) + wave * (32 * 36);
-  const int er = lane >> 3;        // row within an 8-row group
-  const int ec = (lane & 7) * 4;   // first of 4 columns
-#pragma unroll
-  for (int a = 0; a < FN; ++a) {
-#pragma unroll
-    for (int b = 0; b < FM; ++b) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4*>(patch + r32 * 36 + 8 * q + 4 * khalf) =
-            make_float4(acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]);
-      if constexpr (row_store<Epi>()) {
-        const int n = n0 + wn * WN + a * 32 + r32;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = 2 * i + khalf;
-          const float v = patch[row * 36 + r32];
-          const int m = m0 + wm * WM + b * 32 + row;
-          if (m < M && n < N) epi.store1(m, n, v);
-        }
-      } else {
-        f32x4_t v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 t = *reinterpret_cast<const float4*>(patch + (8 * i + er) * 36 + ec);
-          v[i] = f32x4_t{t.x, t.y, t.z, t.w};
-        }
-        const int n = n0 + wn * WN + a * 32 + ec;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = m0 + wm * WM + b * 32 + 8 * i + er;
-          if (m < M && n < N) epi(m, n, v[i]);
-        }
-      }
-    }
-  }
+  tile_epilogue<FM, FN>(acc, lds, epi, M, N, m0 + wm * WM, n0 + wn * WN, wave, lane);
 }
 
-template <int BM, int BN, int BK, int STAGES, class Epi, int WGM = 2, int WGN = 2>
-static void run_bf16_v2(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
+template <int BM, int BN, int BK, int STAGES, class Epi, int WGM, int WGN>
+static void run_bf16_v3(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
                         hipStream_t s) {
   using C = V2Cfg<BM, BN, BK, STAGES, WGM * WGN>;
   static bool attr_set = false;  // one-time, per template instance
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)gemm_bf16_v2_kernel<BM, BN, BK, STAGES, WGM, WGN, Epi>,
+    (void)hipFuncSetAttribute((const void*)gemm_bf16_v3_kernel<BM, BN, BK, STAGES, WGM, WGN, Epi>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
     attr_set = true;
   }
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  gemm_bf16_v2_kernel<BM, BN, BK, STAGES, WGM, WGN, Epi>
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN + (line_aligned<Epi>() ? 1 : 0);
+  gemm_bf16_v3_kernel<BM, BN, BK, STAGES, WGM, WGN, Epi>
       <<<tiles_m * tiles_n, 64 * WGM * WGN, C::LDS_BYTES, s>>>(X, W, M, N, K, epi, tiles_m, tiles_n);
 }
 
@@ -605,12 +736,17 @@ static void dispatch_bf16(const bf16_t* X, const bf16_t* W, int M, int N, int K,
                           hipStream_t s) {
   if (try_skinny(X, W, M, N, K, epi, s))
     return;
-  if (M <= 64)
+  if (M <= 64) {
     run_bf16<64, 64>(X, W, M, N, K, epi, s);
-  else if (K % 64 == 0)
-    run_bf16_v2<128, 192, 64, 2, Epi, 4, 2>(X, W, M, N, K, epi, s);
-  else
+  } else if (K % 64 == 0) {
+    if constexpr (std::is_same_v<Epi, EpiStoreF32>)
+      run_bf16_v3<256, 256, 64, 2, EpiStoreF32Lines, 4, 2>(X, W, M, N, K,
+                                                          EpiStoreF32Lines::make(epi.out, N, M), s);
+    else
+      run_bf16_v3<128, 192, 64, 2, Epi, 4, 2>(X, W, M, N, K, epi, s);
+  } else {
     run_bf16<128, 128>(X, W, M, N, K, epi, s);
+  }
 }
 
 // ================================================================ fp32 FMA kernel

@@ -317,20 +317,23 @@ void launch_attn_rows_f32(const float* q, KvView kv, float* o, int B, int H, int
 }
 
 // ================================================================ decode (bf16, d_h = 64)
-// One workgroup of 16 waves per (sequence, head) streams the whole cache row
-// range 0 .. l_past: wave w takes keys w*64 + 1024*j.  Inside a wave, 8 lanes
-// share a key row (8 dims each) and 8 rows are in flight per pass; a lane
-// issues its 8 K and 8 V row loads together (256 KB in flight per workgroup).
+// One workgroup of NW waves per (sequence, head) streams the whole cache row
+// range 0 .. l_past: wave w takes keys [8 RP (w + NW j), +8 RP).  Inside a
+// wave, 8 lanes share a key row (8 dims each); a lane issues its RP K and RP V
+// row loads together (RP = 16: 32 KB in flight per wave).
 // Each wave keeps an online softmax (running max, partial sums per lane);
-// the 16 waves then merge through LDS, so no second kernel is needed.
-static constexpr int kDecWaves = 16;
+// the waves then merge through LDS, so no second kernel is needed.
+constexpr int kDecWaves = 4, kDecRows = 16;  // measured best at 1024 keys, d_h 64
 
-__global__ __launch_bounds__(1024) void attn_decode_bf16_kernel(const bf16_t* __restrict__ q, KvView kv,
-                                                                bf16_t* __restrict__ o, int H, int nk) {
+// NW waves; RP key rows per lane per pass (RP/8 passes of 8 rows); PF: the
+// next pass's rows are loaded before the current pass is reduced.
+template <int NW, int RP, bool PF>
+__global__ __launch_bounds__(64 * NW) void attn_decode_bf16_kernel(const bf16_t* __restrict__ q, KvView kv,
+                                                                   bf16_t* __restrict__ o, int H, int nk) {
   constexpr int D = 64;
-  __shared__ float wm[kDecWaves];
-  __shared__ float wl[kDecWaves];
-  __shared__ float wo[kDecWaves][D];
+  __shared__ float wm[NW];
+  __shared__ float wl[NW];
+  __shared__ float wo[NW][D];
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh - (bh / H) * H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -345,19 +348,40 @@ __global__ __launch_bounds__(1024) void attn_decode_bf16_kernel(const bf16_t* __
 
   float m = -INFINITY, l = 0.f;
   float ov[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int key0 = wave * 64; key0 < nk; key0 += 64 * kDecWaves) {
-    uint4 kr[8], vr[8];
+  constexpr int KP = 8 * RP;  // keys per wave per pass
+  uint4 kr[RP], vr[RP];
+  auto load = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int key = min(key0 + rg + 8 * i, nk - 1);
+    for (int i = 0; i < RP; ++i) {
+      const int key = min(k0 + rg + 8 * i, nk - 1);
       kr[i] = *reinterpret_cast<const uint4*>(kbase + (long long)key * D + c8 * 8);
       vr[i] = *reinterpret_cast<const uint4*>(vbase + (long long)key * D + c8 * 8);
     }
-    float sv[8];
+  };
+  int key0 = wave * KP;
+  if (PF && key0 < nk) load(key0);
+  for (; key0 < nk; key0 += KP * NW) {
+    uint4 kc[RP], vc[RP];
+    if constexpr (PF) {
+#pragma unroll
+      for (int i = 0; i < RP; ++i) {
+        kc[i] = kr[i];
+        vc[i] = vr[i];
+      }
+      if (key0 + KP * NW < nk) load(key0 + KP * NW);
+    } else {
+      load(key0);
+#pragma unroll
+      for (int i = 0; i < RP; ++i) {
+        kc[i] = kr[i];
+        vc[i] = vr[i];
+      }
+    }
+    float sv[RP];
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint4 u = kr[i];
+    for (int i = 0; i < RP; ++i) {
+      const uint4 u = kc[i];
       float acc = qv[0] * bf_lo(u.x);
       acc = fmaf(qv[1], bf_hi(u.x), acc);
       acc = fmaf(qv[2], bf_lo(u.y), acc);
@@ -382,10 +406,10 @@ __global__ __launch_bounds__(1024) void attn_decode_bf16_kernel(const bf16_t* __
 #pragma unroll
     for (int e = 0; e < 8; ++e) ov[e] *= alpha;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < RP; ++i) {
       const float p = __builtin_amdgcn_exp2f(sv[i] - mnew);  // 0 for masked keys
       l += p;
-      const uint4 u = vr[i];
+      const uint4 u = vc[i];
       ov[0] = fmaf(p, bf_lo(u.x), ov[0]);
       ov[1] = fmaf(p, bf_hi(u.x), ov[1]);
       ov[2] = fmaf(p, bf_lo(u.y), ov[2]);
@@ -415,10 +439,10 @@ __global__ __launch_bounds__(1024) void attn_decode_bf16_kernel(const bf16_t* __
   if (tid < D) {
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, wm[w]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w]);
     float L = 0.f, acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float f = __builtin_amdgcn_exp2f(wm[w] - M);
       L = fmaf(wl[w], f, L);
       acc = fmaf(wo[w][tid], f, acc);
@@ -429,7 +453,7 @@ __global__ __launch_bounds__(1024) void attn_decode_bf16_kernel(const bf16_t* __
 
 void launch_attn_decode_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int l_past,
                              hipStream_t s) {
-  attn_decode_bf16_kernel<<<B * H, 64 * kDecWaves, 0, s>>>(q, kv, o, H, l_past + 1);
+  attn_decode_bf16_kernel<kDecWaves, kDecRows, false><<<B * H, 64 * kDecWaves, 0, s>>>(q, kv, o, H, l_past + 1);
 }
 
 }  // namespace gpt2

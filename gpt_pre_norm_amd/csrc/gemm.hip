@@ -344,7 +344,7 @@ struct V2Cfg {
   static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_U4 * 16 + (DUMMY ? 1024 : 0);
   static_assert(BK == 32 || BK == 64, "BK");
   static_assert(ROWS % RPL == 0, "tile rows fill whole wave loads");
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "wave tiles are multiples of 32");
+  static_assert(BM % 32 == 0 && BN % 32 == 0, "tiles are multiples of 32");
   static_assert((size_t)NW * 32 * 36 * 4 <= LDS_BYTES, "epilogue patches fit in the stage ring");
   static GPT2_DEV int swz(int row, int c) { return c ^ ((row >> SWZ_SHIFT) & (CH - 1)); }
 };
@@ -463,6 +463,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_v3_kernel(const bf16
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int KS = BK / 16;  // MFMA steps per stage
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tiles are multiples of 32");
   static_assert(KS % 2 == 0, "fragment double buffer assumes an even step count");
   extern __shared__ uint4 lds[];
 
@@ -526,18 +527,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_v3_kernel(const bf16
     }
   };
   // The MFMAs of one K step (fragments in `buf`) with the fragment reads of
-  // the next step (into the other buffer) spread between them.  Reads are
-  // issued after the MFMAs they must not delay, so every wait the compiler
-  // places before an MFMA is for reads that have had a whole step to land.
+  // the next step (into the other buffer) between them: issued after the
+  // step's first MFMAs (so the compiler's wait before those covers only reads
+  // that have had a whole step to land) and early enough that the rest of
+  // the step's MFMAs hide their latency.
   auto step = [&](int buf, const uint4* nst, int nks) {
     constexpr int NM = FN * FM, NL = FM + FN;
+    constexpr int SPREAD = NM > 2 ? NM / 2 : NM;  // MFMAs that the reads follow
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       acc[i / FM][i % FM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][i / FM], xf[buf][i % FM],
                                                                     acc[i / FM][i % FM], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
+      if (i < SPREAD) {
 #pragma unroll
-      for (int l = i * NL / NM; l < (i + 1) * NL / NM; ++l) ldone(buf ^ 1, nst, nks, l);
+        for (int l = i * NL / SPREAD; l < (i + 1) * NL / SPREAD; ++l) ldone(buf ^ 1, nst, nks, l);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -734,9 +739,14 @@ static bool try_skinny(const bf16_t* X, const bf16_t* W, int M, int N, int K, co
 template <class Epi>
 static void dispatch_bf16(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
                           hipStream_t s) {
-  if (try_skinny(X, W, M, N, K, epi, s))
-    return;
   if (M <= 64) {
+    // wide outputs (the head): enough 64x128 tiles to stream W over every CU,
+    // X read once per tile instead of once per 32 columns
+    if (N >= 8192 && K % 64 == 0) {
+      run_bf16_v3<64, 128, 64, 2, Epi, 2, 4>(X, W, M, N, K, epi, s);
+      return;
+    }
+    if (try_skinny(X, W, M, N, K, epi, s)) return;
     run_bf16<64, 64>(X, W, M, N, K, epi, s);
   } else if (K % 64 == 0) {
     if constexpr (std::is_same_v<Epi, EpiStoreF32>)

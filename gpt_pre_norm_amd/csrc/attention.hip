@@ -58,7 +58,7 @@ GPT2_DEV int v_swz(int key) { return ((key >> 1) & 1) << 2; }
 
 __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __restrict__ q,
                                                                 KvView kv, bf16_t* __restrict__ o,
-                                                                int H, int T, int nqb) {
+                                                                int H, int T, int l_past, int nqb) {
   constexpr int D = 64;
   __shared__ uint4 lds[kAttnStages * kAttnStageU4];  // 64 KB
 
@@ -68,12 +68,14 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, kh = lane >> 5;
 
+  // queries are rows t of this call; query t sits at position l_past + t and
+  // keys are cache slots (absolute positions)
   const int q0 = qb * 128;
-  const int qw0 = q0 + wave * 32;          // this wave's first query
-  const int kend = min(q0 + 128, T);       // keys needed by the workgroup
+  const int qw0 = q0 + wave * 32;                   // this wave's first query row
+  const int kend = l_past + min(q0 + 128, T);       // keys needed by the workgroup
   const int nkb = (kend + 63) / 64;
-  const int wave_last = min(qw0 + 31, T - 1);
-  const int qpos = qw0 + l32;              // this lane's query position
+  const int wave_last = l_past + min(qw0 + 31, T - 1);  // its last query's position
+  const int qpos = l_past + qw0 + l32;              // this lane's query position
 
   const bf16_t* kbase = (const bf16_t*)kv.base + b * kv.sb + h * kv.sh;
   const bf16_t* vbase = kbase + kv.skv;
@@ -135,7 +137,9 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
     if (ahead >= 2) attn_wait_vmcnt<8>();
     else if (ahead == 1) attn_wait_vmcnt<4>();
     else attn_wait_vmcnt<0>();
-    __syncthreads();
+    // (own loads of tile kb done; a barrier that waits only for LDS
+    // instructions, as __syncthreads() would also drain the tiles in flight)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (kb + kAttnStages - 1 < nkb) issue(kb + kAttnStages - 1, (kb + kAttnStages - 1) % kAttnStages);
     const uint4* ks = lds + (kb % kAttnStages) * kAttnStageU4;
     const uint4* vs = ks + 512;
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
       // units): weights are then at most 2^8, exact in fp32 and in bf16's range,
       // and the O / sum rescale is skipped for most tiles.  Both use the same
       // mref, so the final O / sum is the softmax.
-      if (key0 + 63 > qw0) {
+      if (key0 + 63 > l_past + qw0) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -240,10 +244,11 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
   }
 }
 
-void launch_attn_prefill_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int T, hipStream_t s) {
+void launch_attn_prefill_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int T, int l_past,
+                              hipStream_t s) {
   const int nqb = (T + 127) / 128;
   dim3 grid(B * H, nqb);
-  attn_prefill_bf16_kernel<<<grid, 256, 0, s>>>(q, kv, o, H, T, nqb);
+  attn_prefill_bf16_kernel<<<grid, 256, 0, s>>>(q, kv, o, H, T, l_past, nqb);
 }
 
 // ================================================================ row-wise (fp32)

@@ -180,7 +180,7 @@ struct Run {
     } else if (decode) {
       timed(K_ATTN_DECODE, s, [&] { launch_attn_decode_bf16((const bf16_t*)q, kv, (bf16_t*)o, B, H, l_past, s); });
     } else {
-      timed(K_ATTN_PREFILL, s, [&] { launch_attn_prefill_bf16((const bf16_t*)q, kv, (bf16_t*)o, B, H, T, s); });
+      timed(K_ATTN_PREFILL, s, [&] { launch_attn_prefill_bf16((const bf16_t*)q, kv, (bf16_t*)o, B, H, T, l_past, s); });
     }
     // c_proj + bias + residual -> x1 (fp32)
     Epilogue p{};
@@ -320,6 +320,24 @@ gpt2_status gpt2_decode_step(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_
   if (l_past >= cache->capacity) return GPT2_E_POSITION;
   (void)hipGetLastError();
   Run r{*hp, mode, B, 1, l_past, true, (char*)ws, layout(*hp, mode, B, 1), (hipStream_t)stream};
+  r.model(*W, ids, logits, cache);
+  return hip_status();
+}
+
+gpt2_status gpt2_prefill(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_weights* W,
+                         const int32_t* ids, int32_t B, int32_t T, int32_t l_past, const gpt2_kv* cache,
+                         float* logits, void* ws, size_t ws_bytes, void* stream) {
+  gpt2_status st = check_hparams(hp, mode, true);
+  if (st != GPT2_OK) return st;
+  if (!ids || !logits || !cache) return GPT2_E_NULL;
+  if (!cache->data) return GPT2_E_NULL;
+  if ((st = check_weights(*hp, W)) != GPT2_OK) return st;
+  st = check_common(*hp, mode, B, T, l_past, ws, ws_bytes);
+  if (st != GPT2_OK) return st;
+  if ((long long)l_past + T > cache->capacity) return GPT2_E_POSITION;
+  (void)hipGetLastError();
+  // one new token per sequence is the decode step (its attention kernel)
+  Run r{*hp, mode, B, T, l_past, T == 1, (char*)ws, layout(*hp, mode, B, T), (hipStream_t)stream};
   r.model(*W, ids, logits, cache);
   return hip_status();
 }

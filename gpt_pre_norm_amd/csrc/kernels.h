@@ -55,7 +55,8 @@ void launch_gemm(bool bf16, const void* X, const void* W, int M, int N, int K, c
 // against keys 0 .. l_past+T-1 from the K/V view; q [B, h, T, d_h];
 // o [B, T, h*d_h] (act dtype).
 // Prefill (bf16, d_h == 64, no past): flash kernel with MFMA.
-void launch_attn_prefill_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int T, hipStream_t s);
+void launch_attn_prefill_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int T, int l_past,
+                              hipStream_t s);
 // Row-wise reference-style kernel (fp32 mode, any T, d_h % 4 == 0, d_h <= 128).
 void launch_attn_rows_f32(const float* q, KvView kv, float* o, int B, int H, int T, int d_head,
                           int l_past, hipStream_t s);

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libgpt2mi.so")
 FP32, BF16 = 0, 1
 STATUS = {0: "GPT2_OK", 1: "GPT2_E_NULL", 2: "GPT2_E_SHAPE", 3: "GPT2_E_DTYPE",
           4: "GPT2_E_POSITION", 5: "GPT2_E_WORKSPACE", 6: "GPT2_E_TOKEN", 7: "GPT2_E_HIP"}
-EXPORTS = ("gpt2_workspace_size", "gpt2_block_forward", "gpt2_forward", "gpt2_decode_step",
+EXPORTS = ("gpt2_workspace_size", "gpt2_block_forward", "gpt2_forward", "gpt2_prefill", "gpt2_decode_step",
            "gpt2_read_device_flags", "gpt2_timing_begin", "gpt2_timing_end", "gpt2_status_str")
 BLOCK_KEYS = ("ln1_g", "ln1_b", "attn_w", "attn_b", "proj_w", "proj_b",
               "ln2_g", "ln2_b", "fc_w", "fc_b", "fc2_w", "fc2_b")
@@ -72,6 +72,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        vp, vp, sz, vp]
     lib.gpt2_forward.argtypes = [hp_p, ctypes.c_int, ctypes.POINTER(Weights), vp, i32, i32, vp,
                                  ctypes.POINTER(KV), vp, sz, vp]
+    lib.gpt2_prefill.argtypes = [hp_p, ctypes.c_int, ctypes.POINTER(Weights), vp, i32, i32, i32,
+                                 ctypes.POINTER(KV), vp, vp, sz, vp]
     lib.gpt2_decode_step.argtypes = [hp_p, ctypes.c_int, ctypes.POINTER(Weights), vp, i32, i32,
                                      ctypes.POINTER(KV), vp, vp, sz, vp]
     lib.gpt2_read_device_flags.argtypes = [vp, vp]
@@ -81,7 +83,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gpt2_timing_end.restype = i32
     lib.gpt2_status_str.argtypes = [ctypes.c_int]
     lib.gpt2_status_str.restype = ctypes.c_char_p
-    for f in ("gpt2_block_forward", "gpt2_forward", "gpt2_decode_step", "gpt2_read_device_flags"):
+    for f in ("gpt2_block_forward", "gpt2_forward", "gpt2_prefill", "gpt2_decode_step", "gpt2_read_device_flags"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -174,6 +176,15 @@ def forward(hp: HParams, mode: int, W: ModelWeights, ids, B: int, T: int, logits
     _check(load().gpt2_forward(ctypes.byref(hp), mode, ctypes.byref(W.struct), _ptr(ids), B, T,
                                _ptr(logits), ctypes.byref(kv) if kv is not None else None, _ptr(ws),
                                ws_bytes, _stream(stream)), "gpt2_forward")
+
+
+def prefill(hp: HParams, mode: int, W: ModelWeights, ids, B: int, T: int, l_past: int, cache, capacity: int,
+            logits, ws=None, stream=None, ws_bytes=None):
+    ws_bytes = ws.numel() if ws_bytes is None and ws is not None else (ws_bytes or 0)
+    kv = KV(_ptr(cache), capacity)
+    _check(load().gpt2_prefill(ctypes.byref(hp), mode, ctypes.byref(W.struct), _ptr(ids), B, T, l_past,
+                               ctypes.byref(kv), _ptr(logits), _ptr(ws), ws_bytes, _stream(stream)),
+           "gpt2_prefill")
 
 
 def decode_step(hp: HParams, mode: int, W: ModelWeights, ids, B: int, l_past: int, cache, capacity: int,

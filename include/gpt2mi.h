@@ -27,7 +27,7 @@
  *     (y = x W^T + b); wte is [n_vocab, n_embd], wpe is [n_ctx, n_embd].
  *   - GPT2_BF16: weights, LayerNorm gains/biases, linear biases, block-mode x and y
  *     and the K/V cache are bfloat16; matrix products accumulate in fp32; the
- *     residual stream inside gpt2_forward / gpt2_decode_step is fp32; logits are
+ *     residual stream inside gpt2_forward / gpt2_prefill / gpt2_decode_step is fp32; logits are
  *     fp32.  GPT2_FP32: every tensor is fp32 and all arithmetic is fp32.
  *   - Argument errors are detected on the host before anything is enqueued and
  *     are returned as a status; nothing is launched then.  A launch failure is
@@ -93,8 +93,8 @@ typedef struct {
   int32_t capacity;
 } gpt2_kv;
 
-/* Bytes of workspace any of the three compute calls needs for batch B and
- * T new tokens per sequence (T = 1 for gpt2_decode_step).  0 on bad arguments.
+/* Bytes of workspace any of the compute calls needs for batch B and T new
+ * tokens per sequence (T = 1 for gpt2_decode_step).  0 on bad arguments.
  * A new workspace must be zero-filled once before its first use (the first
  * 256 bytes hold the sticky device flags). */
 size_t gpt2_workspace_size(const gpt2_hparams *hp, gpt2_mode mode, int32_t B, int32_t T);
@@ -124,6 +124,21 @@ gpt2_status gpt2_forward(const gpt2_hparams *hp, gpt2_mode mode, const gpt2_weig
 gpt2_status gpt2_decode_step(const gpt2_hparams *hp, gpt2_mode mode, const gpt2_weights *W,
                              const int32_t *ids, int32_t B, int32_t l_past, const gpt2_kv *cache,
                              float *logits, void *ws, size_t ws_bytes, void *stream);
+
+/* Forward over T new tokens per sequence against a cached past ("Full Forward
+ * Pass", How it works: the model takes the past keys/values and new tokens, and
+ * query t at position l_past + t attends to every key at positions
+ * 0..l_past + t): ids [B, T] int32 (device) at positions l_past..l_past+T-1;
+ * the cache holds slots 0..l_past-1 of every layer and receives the new K, V at
+ * slots l_past..l_past+T-1; logits [B, T, n_vocab] fp32 (device).  Calling it
+ * on consecutive chunks of a sequence fills the cache like one call on the
+ * whole sequence (chunked prefill); l_past = 0 is gpt2_forward with a cache,
+ * T = 1 is gpt2_decode_step.  Requires T >= 1, l_past >= 0 and
+ * l_past + T <= min(n_ctx, cache->capacity), else GPT2_E_POSITION; the
+ * workspace is sized by gpt2_workspace_size(hp, mode, B, T). */
+gpt2_status gpt2_prefill(const gpt2_hparams *hp, gpt2_mode mode, const gpt2_weights *W,
+                         const int32_t *ids, int32_t B, int32_t T, int32_t l_past, const gpt2_kv *cache,
+                         float *logits, void *ws, size_t ws_bytes, void *stream);
 
 /* Synchronises `stream`, then reads and clears the workspace's sticky device
  * flags: GPT2_E_TOKEN if any earlier call on this workspace saw a token id

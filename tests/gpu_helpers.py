@@ -103,3 +103,15 @@ def run_decode(mode, hp, Wdev, ids, l_past, cache, capacity):
 
 def new_cache(mode, B, L, h, cap, dh):
     return torch.zeros((B, L, 2, h, cap, dh), dtype=act_dtype(mode), device="cuda")
+
+
+def run_prefill(mode, hp, Wdev, ids, l_past, cache, capacity):
+    """gpt2_prefill of ids [B, T] at positions l_past.. against the cache."""
+    B, T = ids.shape
+    idd = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
+    logits = torch.empty((B, T, hp.n_vocab), dtype=torch.float32, device="cuda")
+    ws = G.workspace(hp, mode, B, T)
+    G.prefill(hp, mode, Wdev, idd, B, T, l_past, cache, capacity, logits, ws=ws)
+    torch.cuda.synchronize()
+    st = G.read_device_flags(ws)
+    return logits, st

@@ -105,3 +105,25 @@ def test_decode_and_forward_position_errors():
     hp0 = G.hparams(n_vocab=0)
     assert lib.gpt2_forward(ctypes.byref(hp0), G.BF16, ctypes.byref(W), FAKE, 2, 4, FAKE, None, FAKE, big,
                             None) == 2
+
+
+def test_prefill_argument_errors():
+    lib = G.load()
+    hp = G.hparams(n_ctx=1024, n_layer=2)
+    blocks = (G.BlockWeights * 2)(_block_weights(), _block_weights())
+    W = G.Weights(FAKE, FAKE, FAKE, FAKE, ctypes.cast(blocks, ctypes.POINTER(G.BlockWeights)))
+    kv = G.KV(FAKE, 1024)
+    small = G.KV(FAKE, 600)
+    big = 1 << 40
+
+    def call(B, T, l_past, cache, ws_bytes=big):
+        return lib.gpt2_prefill(ctypes.byref(hp), G.BF16, ctypes.byref(W), FAKE, B, T, l_past,
+                                ctypes.byref(cache) if cache is not None else None, FAKE, FAKE, ws_bytes, None)
+
+    # positions l_past .. l_past + T - 1 must stay below n_ctx and the capacity
+    assert call(2, 25, 1000, kv) == 4
+    assert call(2, 100, 512, small) == 4
+    assert call(2, 10, -1, kv) == 4
+    assert call(2, 0, 10, kv) == 2
+    assert call(2, 10, 10, None) == 1
+    assert call(2, 10, 10, kv, ws_bytes=16) == 5

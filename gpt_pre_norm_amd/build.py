@@ -23,6 +23,10 @@ HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
     # no packed-fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: left to itself the compiler parked the
+    # attention's accumulators in AGPRs and copied them back and forth every
+    # key tile (96 v_accvgpr moves per tile per wave)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-result", "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -67,6 +67,52 @@ GPT2_DEV float wave_max(float v) {
   return v;
 }
 
+// LayerNorm of one row by one wave ("GPT-2 Transformer block", norm()
+// excerpt): mean, biased variance of the deviations (two passes over the row
+// held in registers), (x - mean) / sqrt(var + eps), then gain and bias.
+// Lane l holds elements 4(l + 64 i) .. +3, i < NV (zeros past d); requires
+// d <= 256 NV, d % 4 == 0.
+template <int NV, typename Tact>
+GPT2_DEV void ln_row_regs(const float4 (&v)[NV], const Tact* __restrict__ g, const Tact* __restrict__ b,
+                          Tact* __restrict__ yr, int d, float eps, int lane) {
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  const float inv_d = 1.0f / (float)d;
+  const float mean = wave_sum(sum) * inv_d;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = (lane + 64 * i) * 4;
+    if (c < d) {
+      const float a0 = v[i].x - mean, a1 = v[i].y - mean, a2 = v[i].z - mean, a3 = v[i].w - mean;
+      sq += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(sq) * inv_d + eps);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = (lane + 64 * i) * 4;
+    if (c < d) {
+      const float4 gg = load4(g + c), bb = load4(b + c);
+      store4(yr + c, make_float4((v[i].x - mean) * rstd * gg.x + bb.x, (v[i].y - mean) * rstd * gg.y + bb.y,
+                                 (v[i].z - mean) * rstd * gg.z + bb.z, (v[i].w - mean) * rstd * gg.w + bb.w));
+    }
+  }
+}
+
+template <int NV, typename Tin, typename Tact>
+GPT2_DEV void ln_row_wave(const Tin* __restrict__ xr, const Tact* __restrict__ g, const Tact* __restrict__ b,
+                          Tact* __restrict__ yr, int d, float eps, int lane) {
+  float4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = (lane + 64 * i) * 4;
+    v[i] = c < d ? load4(xr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  ln_row_regs<NV>(v, g, b, yr, d, eps, lane);
+}
+
 // GELU, tanh approximation: 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
 // Evaluated through the identity 1 + tanh(u) = 2 / (1 + exp(-2u)), i.e.
 // x / (1 + 2^(-2u log2 e)), with the hardware exp2 and reciprocal (about 1 ulp

@@ -151,8 +151,9 @@ struct Run {
 
   // One pre-norm block.  x_in: block input (fp32 if x_in_f32, else act dtype);
   // x1: fp32 stream after the attention residual; y: block output.
+  // ln1_done: a already holds LN1(x_in).
   void block(const gpt2_block_weights& w, const void* x_in, bool x_in_f32, float* x1, void* y,
-             bool y_f32, KvView kv) const {
+             bool y_f32, KvView kv, bool ln1_done = false) const {
     const int d = hp.n_embd, H = hp.n_head, dh = d / H, m = M();
     const bool b16 = bf16();
     void* a = at(L.a);
@@ -160,7 +161,8 @@ struct Run {
     void* o = at(L.o);
     void* u = at(L.u);
     // LN1
-    timed(K_LAYERNORM, s, [&] { launch_layernorm(x_in_f32 || !b16, b16, x_in, w.ln1_g, w.ln1_b, a, m, d, hp.eps, s); });
+    if (!ln1_done)
+      timed(K_LAYERNORM, s, [&] { launch_layernorm(x_in_f32 || !b16, b16, x_in, w.ln1_g, w.ln1_b, a, m, d, hp.eps, s); });
     // c_attn: q to [B,H,T,dh], k/v into the view at positions l_past..
     Epilogue e{};
     e.kind = EPI_QKV;
@@ -236,12 +238,16 @@ struct Run {
     const int d = hp.n_embd, m = M();
     const bool b16 = bf16();
     float* x = (float*)at(L.x);
-    timed(K_EMBED, s, [&] { launch_embed(b16, ids, W.wte, W.wpe, x, m, T, l_past, d, hp.n_vocab, (uint32_t*)ws, s); });
+    void* a = at(L.a);
+    // embedding and the first block's LN1 in one pass
+    timed(K_EMBED, s, [&] {
+      launch_embed_ln(b16, ids, W.wte, W.wpe, x, W.blocks[0].ln1_g, W.blocks[0].ln1_b, a, m, T, l_past, d,
+                      hp.n_vocab, hp.eps, (uint32_t*)ws, s);
+    });
     for (int l = 0; l < hp.n_layer; ++l) {
       const KvView kv = cache ? cache_view(cache->data, cache->capacity, l) : present_view(at(L.kv));
-      block(W.blocks[l], x, true, x, x, true, kv);
+      block(W.blocks[l], x, true, x, x, true, kv, l == 0);
     }
-    void* a = at(L.a);
     timed(K_LAYERNORM, s, [&] { launch_layernorm(true, b16, x, W.lnf_g, W.lnf_b, a, m, d, hp.eps, s); });
     Epilogue e{};
     e.kind = EPI_STORE_F32;

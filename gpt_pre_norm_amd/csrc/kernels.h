@@ -11,10 +11,12 @@
 namespace gpt2 {
 
 // ---------------------------------------------------------------- embedding
-// x[m, :] = wte[ids[m], :] + wpe[l_past + m % T, :]  (fp32 out); a bad id
-// zero-fills the row and ORs 1 into *flags.
-void launch_embed(bool bf16, const int32_t* ids, const void* wte, const void* wpe, float* x,
-                  int M, int T, int l_past, int d, int n_vocab, uint32_t* flags, hipStream_t s);
+// Embedding plus the first LayerNorm: x[m, :] (fp32) = wte[ids[m], :] +
+// wpe[l_past + m % T, :] and a = LN(x; g, b) in the act dtype, one pass per
+// row; a bad id zero-fills the row and ORs 1 into *flags.
+void launch_embed_ln(bool bf16, const int32_t* ids, const void* wte, const void* wpe, float* x,
+                     const void* g, const void* b, void* a, int M, int T, int l_past, int d, int n_vocab,
+                     float eps, uint32_t* flags, hipStream_t s);
 
 // ---------------------------------------------------------------- LayerNorm
 // y = LN(x) * g + b over rows of width d; one row per wave.
@@ -42,6 +44,7 @@ struct Epilogue {
   KvView kv;          // K/V destination for positions l_past .. l_past + T - 1
   int T, l_past, n_head, d_head, d;
 };
+
 
 // Y = X W^T with the epilogue; X [M, K], W [N, K] row-major.
 // bf16: MFMA paths (K % 8 == 0; M <= 64 uses the weight-streaming skinny

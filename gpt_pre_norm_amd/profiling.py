@@ -50,7 +50,7 @@ def short_name(name: str) -> str:
 def kind_of(name: str, prev_kind: str | None) -> str:
     """Maps a kernel symbol to the kind names gpt2_timing_end reports."""
     n = short_name(name)
-    if "embed_kernel" in n:
+    if "embed" in n:
         return "embed"
     if "layernorm_kernel" in n:
         return "layernorm"
@@ -94,8 +94,9 @@ def classify(rows):
     prev = None
     phase = "forward"
     for did, name, grid, val in rows:
-        # the decode step starts with its embedding of 64 tokens (a small grid)
-        if ("embed_kernel" in name and grid < 1_000_000) or "skinny" in name or "attn_decode" in name:
+        # the decode step starts with its embedding of 64 tokens (64 one-wave
+        # workgroups: a small grid)
+        if ("embed" in name and grid < 65536) or "skinny" in name or "attn_decode" in name:
             phase = "decode"
         k = kind_of(name, prev)
         out.append((did, phase, k, grid, val))

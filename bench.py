@@ -165,6 +165,9 @@ def main():
     del logits, ws
     torch.cuda.empty_cache()
 
+    # ------------------------------------------------------------ chunked prefill
+    result["prefill_chunk"] = bench_prefill_chunk(args, G, R, wl, Wd, hp, ids, stream, dev)
+
     # ------------------------------------------------------------ decode workload
     if not args.no_decode:
         result["decode"] = bench_decode(args, G, R, synth, WORKLOADS["gpt2s_decode_b64_p1023"], Wd, hp,
@@ -175,6 +178,49 @@ def main():
         result["cpu_baseline"] = cpu_baseline(wl, ids_np, W)
 
     print(json.dumps(result), flush=True)
+
+
+def _timed_loop(fn, n):
+    import torch
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(n):
+        fn()
+    ev1.record()
+    torch.cuda.synchronize()
+    return max((time.perf_counter() - t0) * 1e3, ev0.elapsed_time(ev1)) / n
+
+
+def bench_prefill_chunk(args, G, R, wl, Wd, hp, ids, stream, dev):
+    """The forward workload's second half, 512 new tokens per sequence at
+    positions 512..1023, prefilled against the cache that the first half
+    filled (rerunning it rewrites the same slots with the same values)."""
+    import torch
+
+    half = wl.T // 2
+    cache = torch.zeros((wl.B, wl.L, 2, wl.h, wl.n_ctx, wl.dh), dtype=torch.bfloat16, device=dev)
+    logits = torch.empty((wl.B, half, wl.n_vocab), dtype=torch.float32, device=dev)
+    ws = G.workspace(hp, G.BF16, wl.B, half)
+    first, second = ids[:, :half].contiguous(), ids[:, half:].contiguous()
+    G.prefill(hp, G.BF16, Wd, first, wl.B, half, 0, cache, wl.n_ctx, logits, ws=ws, stream=stream)
+
+    def chunk():
+        G.prefill(hp, G.BF16, Wd, second, wl.B, half, half, cache, wl.n_ctx, logits, ws=ws, stream=stream)
+
+    for _ in range(max(1, args.warmup)):
+        chunk()
+    ms = _timed_loop(chunk, args.steps)
+    flops = R.model_flops(wl.B, half, wl.d, wl.h, wl.L, wl.n_vocab) + 4.0 * wl.d * wl.B * half * half * wl.L
+    log(f"[bench] prefill chunk (512 tokens at 512..1023, B={wl.B}) {ms:.3f} ms, "
+        f"{wl.B * half / (ms / 1e3):.4g} tok/s, {flops / (ms / 1e3) / 1e12:.1f} TFLOP/s")
+    del cache, logits, ws
+    torch.cuda.empty_cache()
+    return {"value": round(wl.B * half / (ms / 1e3), 1), "unit": "tokens/s", "ms": round(ms, 4),
+            "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+            "workload": "GPT-2 small, B=8, 512 new tokens per sequence at positions 512..1023 "
+                        "against a cache holding positions 0..511 (gpt2_prefill)"}
 
 
 def bench_decode(args, G, R, synth, wl, Wd, hp, stream, dev):
@@ -203,16 +249,7 @@ def bench_decode(args, G, R, synth, wl, Wd, hp, stream, dev):
         step()
     torch.cuda.synchronize()
 
-    def timed_loop(fn, n):
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        ev0.record()
-        for _ in range(n):
-            fn()
-        ev1.record()
-        torch.cuda.synchronize()
-        return max((time.perf_counter() - t0) * 1e3, ev0.elapsed_time(ev1)) / n
+    timed_loop = _timed_loop
 
     ms_eager = timed_loop(step, args.decode_steps)
     # the same step captured once into a HIP graph and replayed (the ~100
@@ -245,6 +282,24 @@ def bench_decode(args, G, R, synth, wl, Wd, hp, stream, dev):
     n, tot = kt[dom]
     avg_s = tot / n / 1e3
     ach = b / avg_s / 1e9
+
+    # greedy generation: 32 tokens from position 991 on the same cache (the
+    # loop rewrites slots 991..1022 with the same values on every run)
+    n_new, start = 32, wl.l_past - 32
+    out = torch.empty((wl.B, n_new), dtype=torch.int32, device=dev)
+    gws = G.generate_workspace(hp, G.BF16, wl.B)
+
+    def gen():
+        G.generate_greedy(hp, G.BF16, Wd, ids, wl.B, start, n_new, cache, cap, out, ws=gws, stream=stream)
+
+    gen()
+    gen_ms = _timed_loop(gen, max(1, args.decode_steps // 10))
+    log(f"[bench] greedy generation {n_new} tokens x {wl.B} sequences from position {start}: "
+        f"{gen_ms:.3f} ms, {wl.B * n_new / (gen_ms / 1e3):.4g} tok/s")
+    generate = {"value": round(wl.B * n_new / (gen_ms / 1e3), 1), "unit": "tokens/s",
+                "ms_per_call": round(gen_ms, 4), "n_new": n_new, "from_position": start,
+                "workload": "GPT-2 small greedy generation (gpt2_generate_greedy), B=64, 32 tokens "
+                            "per sequence from position 991 over the decode workload's past"}
     return {
         "value": round(wl.B / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
         "steps": args.decode_steps, "launch": "hip graph replay of one decode step",
@@ -257,6 +312,7 @@ def bench_decode(args, G, R, synth, wl, Wd, hp, stream, dev):
                      "unit": "GB/s", "frac": round(ach * 1e9 / R.PEAK_HBM_BYTES, 4),
                      "traffic": traffic_for("decode", dom), "work_per_launch": b, "avg_launch_us": round(avg_s * 1e6, 2)},
         "kernels": kernels,
+        "generate": generate,
     }
 
 

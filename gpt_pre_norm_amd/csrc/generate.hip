@@ -1,0 +1,61 @@
+// Greedy next-token choice for the generation loop: the argmax of each row of
+// the head's fp32 logits ("Full Forward Pass", How it works: a generation loop
+// feeds the chosen token back; the greedy choice is the most likely token).
+// Ties go to the lowest index; NaN logits are never chosen over a number.
+#include "kernels.h"
+
+namespace gpt2 {
+
+constexpr int kArgmaxThreads = 256;
+
+// One workgroup per row: strided scan, then a wave and an LDS reduction.
+__global__ __launch_bounds__(kArgmaxThreads) void argmax_rows_kernel(const float* __restrict__ logits, int V,
+                                                                      int32_t* __restrict__ next_ids,
+                                                                      int32_t* __restrict__ out, int out_stride,
+                                                                      int step) {
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* row = logits + (long long)b * V;
+  float best = -INFINITY;
+  int bi = V;  // "none": loses every comparison below
+  for (int n = tid; n < V; n += kArgmaxThreads) {
+    const float v = row[n];
+    if (v > best || (v == best && n < bi)) {
+      best = v;
+      bi = n;
+    }
+  }
+  auto better = [](float v, int i, float w, int j) { return w > v || (w == v && j < i); };
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float w = __shfl_xor(best, o, 64);
+    const int j = __shfl_xor(bi, o, 64);
+    if (better(best, bi, w, j)) {
+      best = w;
+      bi = j;
+    }
+  }
+  __shared__ float sv[kArgmaxThreads / 64];
+  __shared__ int si[kArgmaxThreads / 64];
+  if (lane == 0) {
+    sv[wave] = best;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kArgmaxThreads / 64; ++w)
+      if (better(best, bi, sv[w], si[w])) {
+        best = sv[w];
+        bi = si[w];
+      }
+    const int tok = bi < V ? bi : 0;  // an all-NaN row falls back to token 0
+    next_ids[b] = tok;
+    out[(long long)b * out_stride + step] = tok;
+  }
+}
+
+void launch_argmax_rows(const float* logits, int B, int V, int32_t* next_ids, int32_t* out, int out_stride,
+                        int step, hipStream_t s) {
+  argmax_rows_kernel<<<B, kArgmaxThreads, 0, s>>>(logits, V, next_ids, out, out_stride, step);
+}
+
+}  // namespace gpt2

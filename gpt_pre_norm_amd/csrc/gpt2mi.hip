@@ -51,6 +51,23 @@ Layout layout(const gpt2_hparams& hp, gpt2_mode mode, int B, int T) {
   return L;
 }
 
+// Generation: the decode step's regions, then the step's logits [B, V] fp32
+// and the next tokens [B] int32.
+struct GenLayout {
+  Layout step;
+  size_t logits, ids, total;
+};
+
+GenLayout gen_layout(const gpt2_hparams& hp, gpt2_mode mode, int B) {
+  GenLayout G;
+  G.step = layout(hp, mode, B, 1);
+  size_t off = G.step.total;
+  G.logits = off;  off += up((size_t)B * hp.n_vocab * 4);
+  G.ids = off;     off += up((size_t)B * 4);
+  G.total = off;
+  return G;
+}
+
 gpt2_status check_hparams(const gpt2_hparams* hp, gpt2_mode mode, bool need_model) {
   if (!hp) return GPT2_E_NULL;
   if (mode != GPT2_FP32 && mode != GPT2_BF16) return GPT2_E_DTYPE;
@@ -94,11 +111,11 @@ gpt2_status hip_status() { return hipGetLastError() == hipSuccess ? GPT2_OK : GP
 // a HIP event pair on its stream; events are created once and reused.
 enum Kern {
   K_EMBED, K_LAYERNORM, K_GEMM_C_ATTN, K_GEMM_ATTN_PROJ, K_GEMM_C_FC, K_GEMM_MLP_PROJ, K_GEMM_HEAD,
-  K_ATTN_PREFILL, K_ATTN_ROWS, K_ATTN_DECODE, K_COUNT
+  K_ATTN_PREFILL, K_ATTN_ROWS, K_ATTN_DECODE, K_ARGMAX, K_COUNT
 };
 const char* const kKernNames[K_COUNT] = {
     "embed", "layernorm", "gemm_c_attn", "gemm_attn_c_proj", "gemm_c_fc", "gemm_mlp_c_proj",
-    "gemm_lm_head", "attn_prefill", "attn_rows_f32", "attn_decode"};
+    "gemm_lm_head", "attn_prefill", "attn_rows_f32", "attn_decode", "argmax"};
 
 struct Timing {
   bool on = false;
@@ -345,6 +362,39 @@ gpt2_status gpt2_prefill(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_weig
   // one new token per sequence is the decode step (its attention kernel)
   Run r{*hp, mode, B, T, l_past, T == 1, (char*)ws, layout(*hp, mode, B, T), (hipStream_t)stream};
   r.model(*W, ids, logits, cache);
+  return hip_status();
+}
+
+size_t gpt2_generate_workspace_size(const gpt2_hparams* hp, gpt2_mode mode, int32_t B) {
+  if (check_hparams(hp, mode, true) != GPT2_OK) return 0;
+  if (B < 1 || B > kMaxTokens) return 0;
+  return gen_layout(*hp, mode, B).total;
+}
+
+gpt2_status gpt2_generate_greedy(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_weights* W,
+                                 const int32_t* ids, int32_t B, int32_t l_past, int32_t n_new,
+                                 const gpt2_kv* cache, int32_t* out, void* ws, size_t ws_bytes, void* stream) {
+  gpt2_status st = check_hparams(hp, mode, true);
+  if (st != GPT2_OK) return st;
+  if (!ids || !out || !cache || !ws) return GPT2_E_NULL;
+  if (!cache->data) return GPT2_E_NULL;
+  if ((st = check_weights(*hp, W)) != GPT2_OK) return st;
+  if (B < 1 || n_new < 1 || B > kMaxTokens) return GPT2_E_SHAPE;
+  if (l_past < 0 || (long long)l_past + n_new > hp->n_ctx || (long long)l_past + n_new > cache->capacity)
+    return GPT2_E_POSITION;
+  if (mode == GPT2_FP32 && l_past + n_new > kMaxRowKeysF32) return GPT2_E_SHAPE;
+  const GenLayout G = gen_layout(*hp, mode, B);
+  if (ws_bytes < G.total) return GPT2_E_WORKSPACE;
+  (void)hipGetLastError();
+  char* w = (char*)ws;
+  float* logits = (float*)(w + G.logits);
+  int32_t* next = (int32_t*)(w + G.ids);
+  for (int i = 0; i < n_new; ++i) {
+    // token i sits at position l_past + i; its logits choose token i + 1
+    Run r{*hp, mode, B, 1, l_past + i, true, w, G.step, (hipStream_t)stream};
+    r.model(*W, i == 0 ? ids : next, logits, cache);
+    timed(K_ARGMAX, r.s, [&] { launch_argmax_rows(logits, B, hp->n_vocab, next, out, n_new, i, r.s); });
+  }
   return hip_status();
 }
 

@@ -67,4 +67,10 @@ void launch_attn_rows_f32(const float* q, KvView kv, float* o, int B, int H, int
 void launch_attn_decode_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int l_past,
                              hipStream_t s);
 
+// ---------------------------------------------------------------- generation
+// next_ids[b] = out[b * out_stride + step] = argmax_n logits[b, n] (lowest
+// index among equal maxima), for b < B.
+void launch_argmax_rows(const float* logits, int B, int V, int32_t* next_ids, int32_t* out, int out_stride,
+                        int step, hipStream_t s);
+
 }  // namespace gpt2

@@ -20,7 +20,8 @@ FP32, BF16 = 0, 1
 STATUS = {0: "GPT2_OK", 1: "GPT2_E_NULL", 2: "GPT2_E_SHAPE", 3: "GPT2_E_DTYPE",
           4: "GPT2_E_POSITION", 5: "GPT2_E_WORKSPACE", 6: "GPT2_E_TOKEN", 7: "GPT2_E_HIP"}
 EXPORTS = ("gpt2_workspace_size", "gpt2_block_forward", "gpt2_forward", "gpt2_prefill", "gpt2_decode_step",
-           "gpt2_read_device_flags", "gpt2_timing_begin", "gpt2_timing_end", "gpt2_status_str")
+           "gpt2_generate_workspace_size", "gpt2_generate_greedy", "gpt2_read_device_flags",
+           "gpt2_timing_begin", "gpt2_timing_end", "gpt2_status_str")
 BLOCK_KEYS = ("ln1_g", "ln1_b", "attn_w", "attn_b", "proj_w", "proj_b",
               "ln2_g", "ln2_b", "fc_w", "fc_b", "fc2_w", "fc2_b")
 
@@ -76,6 +77,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                  ctypes.POINTER(KV), vp, vp, sz, vp]
     lib.gpt2_decode_step.argtypes = [hp_p, ctypes.c_int, ctypes.POINTER(Weights), vp, i32, i32,
                                      ctypes.POINTER(KV), vp, vp, sz, vp]
+    lib.gpt2_generate_workspace_size.argtypes = [hp_p, ctypes.c_int, i32]
+    lib.gpt2_generate_workspace_size.restype = sz
+    lib.gpt2_generate_greedy.argtypes = [hp_p, ctypes.c_int, ctypes.POINTER(Weights), vp, i32, i32, i32,
+                                         ctypes.POINTER(KV), vp, vp, sz, vp]
     lib.gpt2_read_device_flags.argtypes = [vp, vp]
     lib.gpt2_timing_begin.argtypes = []
     lib.gpt2_timing_begin.restype = ctypes.c_int
@@ -83,7 +88,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gpt2_timing_end.restype = i32
     lib.gpt2_status_str.argtypes = [ctypes.c_int]
     lib.gpt2_status_str.restype = ctypes.c_char_p
-    for f in ("gpt2_block_forward", "gpt2_forward", "gpt2_prefill", "gpt2_decode_step", "gpt2_read_device_flags"):
+    for f in ("gpt2_block_forward", "gpt2_forward", "gpt2_prefill", "gpt2_decode_step", "gpt2_generate_greedy",
+              "gpt2_read_device_flags"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -194,6 +200,23 @@ def decode_step(hp: HParams, mode: int, W: ModelWeights, ids, B: int, l_past: in
     _check(load().gpt2_decode_step(ctypes.byref(hp), mode, ctypes.byref(W.struct), _ptr(ids), B, l_past,
                                    ctypes.byref(kv), _ptr(logits), _ptr(ws), ws_bytes, _stream(stream)),
            "gpt2_decode_step")
+
+
+def generate_workspace(hp: HParams, mode: int, B: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for generate_greedy (uint8 tensor)."""
+    n = int(load().gpt2_generate_workspace_size(ctypes.byref(hp), mode, B))
+    if n == 0:
+        raise Gpt2Error(2, "gpt2_generate_workspace_size")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def generate_greedy(hp: HParams, mode: int, W: ModelWeights, ids, B: int, l_past: int, n_new: int, cache,
+                    capacity: int, out, ws=None, stream=None, ws_bytes=None):
+    ws_bytes = ws.numel() if ws_bytes is None and ws is not None else (ws_bytes or 0)
+    kv = KV(_ptr(cache), capacity)
+    _check(load().gpt2_generate_greedy(ctypes.byref(hp), mode, ctypes.byref(W.struct), _ptr(ids), B, l_past,
+                                       n_new, ctypes.byref(kv), _ptr(out), _ptr(ws), ws_bytes, _stream(stream)),
+           "gpt2_generate_greedy")
 
 
 def read_device_flags(ws, stream=None) -> int:

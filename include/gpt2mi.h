@@ -140,6 +140,25 @@ gpt2_status gpt2_prefill(const gpt2_hparams *hp, gpt2_mode mode, const gpt2_weig
                          const int32_t *ids, int32_t B, int32_t T, int32_t l_past, const gpt2_kv *cache,
                          float *logits, void *ws, size_t ws_bytes, void *stream);
 
+/* Bytes of workspace gpt2_generate_greedy needs for batch B (0 on bad
+ * arguments); zero-filled once before first use, like the others. */
+size_t gpt2_generate_workspace_size(const gpt2_hparams *hp, gpt2_mode mode, int32_t B);
+
+/* Greedy generation loop ("Full Forward Pass", How it works: each step feeds
+ * only the newest token with the cached keys/values, and the chosen token is
+ * fed back).  ids [B] int32 (device): the token at position l_past of each
+ * sequence, whose cache already holds slots 0..l_past-1.  Runs n_new decode
+ * steps entirely on the device: step i feeds token i at position l_past + i
+ * (appending its K, V at that slot) and picks token i + 1 as the argmax of its
+ * logits (lowest index among equal maxima), written to out[b * n_new + i]
+ * (out: [B, n_new] int32, device).  Nothing is synchronised and no logits are
+ * returned.  Requires n_new >= 1 and l_past + n_new <= min(n_ctx,
+ * cache->capacity), else GPT2_E_POSITION; ws_bytes >=
+ * gpt2_generate_workspace_size(hp, mode, B). */
+gpt2_status gpt2_generate_greedy(const gpt2_hparams *hp, gpt2_mode mode, const gpt2_weights *W,
+                                 const int32_t *ids, int32_t B, int32_t l_past, int32_t n_new,
+                                 const gpt2_kv *cache, int32_t *out, void *ws, size_t ws_bytes, void *stream);
+
 /* Synchronises `stream`, then reads and clears the workspace's sticky device
  * flags: GPT2_E_TOKEN if any earlier call on this workspace saw a token id
  * outside [0, n_vocab), else GPT2_OK (or GPT2_E_HIP). */

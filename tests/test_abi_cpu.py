@@ -127,3 +127,29 @@ def test_prefill_argument_errors():
     assert call(2, 0, 10, kv) == 2
     assert call(2, 10, 10, None) == 1
     assert call(2, 10, 10, kv, ws_bytes=16) == 5
+
+
+def test_generate_argument_errors():
+    lib = G.load()
+    hp = G.hparams(n_ctx=1024, n_layer=2)
+    blocks = (G.BlockWeights * 2)(_block_weights(), _block_weights())
+    W = G.Weights(FAKE, FAKE, FAKE, FAKE, ctypes.cast(blocks, ctypes.POINTER(G.BlockWeights)))
+    kv = G.KV(FAKE, 1024)
+    small = G.KV(FAKE, 600)
+    big = 1 << 40
+
+    def call(B, l_past, n_new, cache, out=FAKE, ws_bytes=big):
+        return lib.gpt2_generate_greedy(ctypes.byref(hp), G.BF16, ctypes.byref(W), FAKE, B, l_past, n_new,
+                                        ctypes.byref(cache) if cache is not None else None, out, FAKE,
+                                        ws_bytes, None)
+
+    assert call(2, 1000, 25, kv) == 4      # positions past n_ctx
+    assert call(2, 590, 20, small) == 4    # past the cache capacity
+    assert call(2, -1, 5, kv) == 4
+    assert call(2, 10, 0, kv) == 2
+    assert call(0, 10, 5, kv) == 2
+    assert call(2, 10, 5, None) == 1
+    assert call(2, 10, 5, kv, out=None) == 1
+    assert call(2, 10, 5, kv, ws_bytes=16) == 5
+    need = G.load().gpt2_generate_workspace_size(ctypes.byref(hp), G.BF16, 2)
+    assert need > G.workspace_size(hp, G.BF16, 2, 1)   # the step's regions plus logits and tokens

@@ -165,8 +165,9 @@ def main():
     del logits, ws
     torch.cuda.empty_cache()
 
-    # ------------------------------------------------------------ chunked prefill
+    # ------------------------------------------------------------ chunked prefill, loss
     result["prefill_chunk"] = bench_prefill_chunk(args, G, R, wl, Wd, hp, ids, stream, dev)
+    result["forward_loss"] = bench_forward_loss(args, G, R, wl, Wd, hp, ids, stream, dev)
 
     # ------------------------------------------------------------ decode workload
     if not args.no_decode:
@@ -221,6 +222,38 @@ def bench_prefill_chunk(args, G, R, wl, Wd, hp, ids, stream, dev):
             "tflops": round(flops / (ms / 1e3) / 1e12, 1),
             "workload": "GPT-2 small, B=8, 512 new tokens per sequence at positions 512..1023 "
                         "against a cache holding positions 0..511 (gpt2_prefill)"}
+
+
+def bench_forward_loss(args, G, R, wl, Wd, hp, ids, stream, dev):
+    """The forward workload with the fused head + next-token cross-entropy
+    (targets = ids shifted by one); no logits are written."""
+    import torch
+
+    targets = torch.cat([ids[:, 1:], ids[:, :1]], dim=1).contiguous()
+    loss = torch.empty((wl.B, wl.T), dtype=torch.float32, device=dev)
+    ws = G.loss_workspace(hp, G.BF16, wl.B, wl.T)
+
+    def run():
+        G.forward_loss(hp, G.BF16, Wd, ids, targets, wl.B, wl.T, loss, ws=ws, stream=stream)
+
+    for _ in range(max(1, args.warmup)):
+        run()
+    ms = _timed_loop(run, args.steps)
+    G.timing_begin()
+    run()
+    kt = G.timing_end()
+    head_us = kt["gemm_lm_head"][1] * 1e3 / kt["gemm_lm_head"][0]
+    loss_us = kt["loss"][1] * 1e3 / kt["loss"][0]
+    flops = R.model_flops(wl.B, wl.T, wl.d, wl.h, wl.L, wl.n_vocab)
+    log(f"[bench] forward + loss {ms:.3f} ms/step, {wl.tokens / (ms / 1e3):.4g} tok/s; fused head {head_us:.1f} us, "
+        f"loss rows {loss_us:.1f} us")
+    del loss, ws
+    torch.cuda.empty_cache()
+    return {"value": round(wl.tokens / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+            "tflops": round(flops / (ms / 1e3) / 1e12, 1), "head_us": round(head_us, 2),
+            "loss_rows_us": round(loss_us, 2),
+            "workload": "GPT-2 small forward B=8 T=1024 with the tied head fused into the next-token "
+                        "cross-entropy (gpt2_forward_loss); per-position losses, no logits written"}
 
 
 def bench_decode(args, G, R, synth, wl, Wd, hp, stream, dev):

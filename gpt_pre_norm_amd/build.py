@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["gpt2mi.hip", "embed_ln.hip", "gemm.hip", "attention.hip", "generate.hip"]
+SOURCES = ["gpt2mi.hip", "embed_ln.hip", "gemm.hip", "attention.hip", "generate.hip", "loss.hip"]
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
     # no packed-fp32 instructions anywhere in the device code

@@ -94,6 +94,22 @@ struct EpiStoreF32Lines {
   }
 };
 
+// The tied head without its logits: per row m and per (column tile, wave
+// column) the partial log-sum-exp state (max, sum of exp(logit - max)) goes to
+// part[m][slot] and the logit of the row's target column to tgt[m]; a row
+// kernel combines them into the next-token cross-entropy (loss_rows_kernel).
+struct EpiLoss {
+  static constexpr bool kRowLse = true;
+  const int32_t* targets;  // [M]
+  float2* part;            // [M][nparts]
+  float* tgt;              // [M]
+  int N, nparts;
+  struct Ctx {};
+  GPT2_DEV Ctx load(int, int) const { return {}; }
+  GPT2_DEV void store(int, int, f32x4_t, Ctx) const {}
+  GPT2_DEV void operator()(int, int, f32x4_t) const {}
+};
+
 template <typename Tact>
 struct EpiBiasGelu {
   const Tact* bias;
@@ -355,6 +371,51 @@ constexpr bool line_aligned() {
 }
 
 template <class Epi>
+constexpr bool row_lse() {
+  if constexpr (requires { Epi::kRowLse; }) return Epi::kRowLse;
+  else return false;
+}
+
+// EpiLoss at the end of a tile, straight from the MFMA layout: lane l holds,
+// for token m = mw0 + 32 b + l%32, the 16 x FN logits of columns
+// nw0 + 32 a + 8 (r/4) + 4 (l/32) + r%4; the two lanes l and l + 32 cover the
+// wave's WN columns of that token.
+template <int FM, int FN, int WN>
+GPT2_DEV void lse_epilogue(const f32x16_t (&acc)[FN][FM], const EpiLoss& epi, int M, int mw0, int nw0,
+                           int slot, int lane) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int r32 = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < FM; ++b) {
+    const int m = mw0 + b * 32 + r32;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int a = 0; a < FN; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = nw0 + a * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+        if (n < epi.N) mx = fmaxf(mx, acc[a][b][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float sm = 0.f;
+    const int t = m < M ? epi.targets[m] : -1;
+#pragma unroll
+    for (int a = 0; a < FN; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = nw0 + a * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+        if (n < epi.N) {
+          sm += __builtin_amdgcn_exp2f((acc[a][b][r] - mx) * kLog2e);
+          if (n == t) epi.tgt[m] = acc[a][b][r];
+        }
+      }
+    sm += __shfl_xor(sm, 32, 64);
+    if (kh == 0 && m < M) epi.part[(long long)m * epi.nparts + slot] = make_float2(mx, sm);
+  }
+  (void)WN;
+}
+
+template <class Epi>
 constexpr bool row_store() {
   if constexpr (requires { Epi::kRowStore; }) return Epi::kRowStore;
   else return false;
@@ -573,8 +634,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_v3_kernel(const bf16
     step(1, lds + ((kt + 1) % STAGES) * C::STAGE_U4, 0);
   }
 
-  __syncthreads();  // all waves are done reading the K stages
-  tile_epilogue<FM, FN>(acc, lds, epi, M, N, m0 + wm * WM, n0 + wn * WN, wave, lane);
+  if constexpr (row_lse<Epi>()) {
+    lse_epilogue<FM, FN, WN>(acc, epi, M, m0 + wm * WM, n0 + wn * WN, tn_idx * WGN + wn, lane);
+  } else {
+    __syncthreads();  // all waves are done reading the K stages
+    tile_epilogue<FM, FN>(acc, lds, epi, M, N, m0 + wm * WM, n0 + wn * WN, wave, lane);
+  }
 }
 
 template <int BM, int BN, int BK, int STAGES, class Epi, int WGM, int WGN>
@@ -847,6 +912,16 @@ static void launch_typed(const Tact* X, const Tact* W, int M, int N, int K, cons
                       FastDiv::make(e.T), FastDiv::make(e.d_head)});
       break;
   }
+}
+
+bool head_lse_fused(bool bf16, int M, int K) { return bf16 && M > 64 && K % 64 == 0; }
+
+int head_lse_parts(int N) { return 2 * ((N + 255) / 256); }
+
+void launch_head_lse(const void* X, const void* W, int M, int N, int K, const int32_t* targets, void* part,
+                     float* tgt, hipStream_t s) {
+  const EpiLoss epi{targets, (float2*)part, tgt, N, head_lse_parts(N)};
+  run_bf16_v3<256, 256, 64, 2, EpiLoss, 4, 2>((const bf16_t*)X, (const bf16_t*)W, M, N, K, epi, s);
 }
 
 void launch_gemm(bool bf16, const void* X, const void* W, int M, int N, int K, const Epilogue& e,

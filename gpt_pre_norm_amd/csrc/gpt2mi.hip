@@ -68,6 +68,31 @@ GenLayout gen_layout(const gpt2_hparams& hp, gpt2_mode mode, int B) {
   return G;
 }
 
+// Loss: the forward's regions, then either the fused head's partial
+// log-sum-exp states and target logits, or full fp32 logits rows.
+struct LossLayout {
+  Layout fwd;
+  bool fused;
+  size_t part, tgt, logits, total;
+};
+
+LossLayout loss_layout(const gpt2_hparams& hp, gpt2_mode mode, int B, int T) {
+  LossLayout G;
+  G.fwd = layout(hp, mode, B, T);
+  const size_t M = (size_t)B * T;
+  G.fused = head_lse_fused(mode == GPT2_BF16, (int)M, hp.n_embd);
+  size_t off = G.fwd.total;
+  G.part = G.tgt = G.logits = 0;
+  if (G.fused) {
+    G.part = off;  off += up(M * head_lse_parts(hp.n_vocab) * 8);
+    G.tgt = off;   off += up(M * 4);
+  } else {
+    G.logits = off;  off += up(M * (size_t)hp.n_vocab * 4);
+  }
+  G.total = off;
+  return G;
+}
+
 gpt2_status check_hparams(const gpt2_hparams* hp, gpt2_mode mode, bool need_model) {
   if (!hp) return GPT2_E_NULL;
   if (mode != GPT2_FP32 && mode != GPT2_BF16) return GPT2_E_DTYPE;
@@ -111,11 +136,11 @@ gpt2_status hip_status() { return hipGetLastError() == hipSuccess ? GPT2_OK : GP
 // a HIP event pair on its stream; events are created once and reused.
 enum Kern {
   K_EMBED, K_LAYERNORM, K_GEMM_C_ATTN, K_GEMM_ATTN_PROJ, K_GEMM_C_FC, K_GEMM_MLP_PROJ, K_GEMM_HEAD,
-  K_ATTN_PREFILL, K_ATTN_ROWS, K_ATTN_DECODE, K_ARGMAX, K_COUNT
+  K_ATTN_PREFILL, K_ATTN_ROWS, K_ATTN_DECODE, K_ARGMAX, K_LOSS, K_COUNT
 };
 const char* const kKernNames[K_COUNT] = {
     "embed", "layernorm", "gemm_c_attn", "gemm_attn_c_proj", "gemm_c_fc", "gemm_mlp_c_proj",
-    "gemm_lm_head", "attn_prefill", "attn_rows_f32", "attn_decode", "argmax"};
+    "gemm_lm_head", "attn_prefill", "attn_rows_f32", "attn_decode", "argmax", "loss"};
 
 struct Timing {
   bool on = false;
@@ -252,6 +277,15 @@ struct Run {
 
   // Embedding, L blocks, ln_f, head.
   void model(const gpt2_weights& W, const int32_t* ids, float* logits, const gpt2_kv* cache) const {
+    trunk(W, ids, cache);
+    Epilogue e{};
+    e.kind = EPI_STORE_F32;
+    e.out = logits;
+    timed(K_GEMM_HEAD, s, [&] { launch_gemm(bf16(), at(L.a), W.wte, M(), hp.n_vocab, hp.n_embd, e, s); });
+  }
+
+  // Embedding, L blocks and ln_f: a holds LN_f(H) afterwards.
+  void trunk(const gpt2_weights& W, const int32_t* ids, const gpt2_kv* cache) const {
     const int d = hp.n_embd, m = M();
     const bool b16 = bf16();
     float* x = (float*)at(L.x);
@@ -266,10 +300,6 @@ struct Run {
       block(W.blocks[l], x, true, x, x, true, kv, l == 0);
     }
     timed(K_LAYERNORM, s, [&] { launch_layernorm(true, b16, x, W.lnf_g, W.lnf_b, a, m, d, hp.eps, s); });
-    Epilogue e{};
-    e.kind = EPI_STORE_F32;
-    e.out = logits;
-    timed(K_GEMM_HEAD, s, [&] { launch_gemm(b16, a, W.wte, m, hp.n_vocab, d, e, s); });
   }
 };
 
@@ -394,6 +424,51 @@ gpt2_status gpt2_generate_greedy(const gpt2_hparams* hp, gpt2_mode mode, const g
     Run r{*hp, mode, B, 1, l_past + i, true, w, G.step, (hipStream_t)stream};
     r.model(*W, i == 0 ? ids : next, logits, cache);
     timed(K_ARGMAX, r.s, [&] { launch_argmax_rows(logits, B, hp->n_vocab, next, out, n_new, i, r.s); });
+  }
+  return hip_status();
+}
+
+size_t gpt2_loss_workspace_size(const gpt2_hparams* hp, gpt2_mode mode, int32_t B, int32_t T) {
+  if (check_hparams(hp, mode, true) != GPT2_OK) return 0;
+  if (B < 1 || T < 1 || (long long)B * T > kMaxTokens) return 0;
+  return loss_layout(*hp, mode, B, T).total;
+}
+
+gpt2_status gpt2_forward_loss(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_weights* W,
+                              const int32_t* ids, const int32_t* targets, int32_t B, int32_t T, float* loss,
+                              const gpt2_kv* present, void* ws, size_t ws_bytes, void* stream) {
+  gpt2_status st = check_hparams(hp, mode, true);
+  if (st != GPT2_OK) return st;
+  if (!ids || !targets || !loss) return GPT2_E_NULL;
+  if ((st = check_weights(*hp, W)) != GPT2_OK) return st;
+  if (present && !present->data) return GPT2_E_NULL;
+  st = check_common(*hp, mode, B, T, 0, ws, 0);
+  if (st != GPT2_OK && st != GPT2_E_WORKSPACE) return st;
+  const LossLayout G = loss_layout(*hp, mode, B, T);
+  if (ws_bytes < G.total) return GPT2_E_WORKSPACE;
+  if (present && present->capacity < T) return GPT2_E_POSITION;
+  (void)hipGetLastError();
+  Run r{*hp, mode, B, T, 0, false, (char*)ws, G.fwd, (hipStream_t)stream};
+  r.trunk(*W, ids, present);
+  char* w = (char*)ws;
+  const int m = B * T, V = hp->n_vocab, d = hp->n_embd;
+  uint32_t* flags = (uint32_t*)ws;
+  if (G.fused) {
+    timed(K_GEMM_HEAD, r.s, [&] {
+      launch_head_lse(r.at(G.fwd.a), W->wte, m, V, d, targets, w + G.part, (float*)(w + G.tgt), r.s);
+    });
+    timed(K_LOSS, r.s, [&] {
+      launch_loss_from_parts(w + G.part, head_lse_parts(V), (const float*)(w + G.tgt), targets, m, V, loss, flags,
+                             r.s);
+    });
+  } else {
+    Epilogue e{};
+    e.kind = EPI_STORE_F32;
+    e.out = w + G.logits;
+    timed(K_GEMM_HEAD, r.s, [&] { launch_gemm(mode == GPT2_BF16, r.at(G.fwd.a), W->wte, m, V, d, e, r.s); });
+    timed(K_LOSS, r.s, [&] {
+      launch_loss_from_logits((const float*)(w + G.logits), targets, m, V, loss, flags, r.s);
+    });
   }
   return hip_status();
 }

@@ -53,6 +53,23 @@ struct Epilogue {
 void launch_gemm(bool bf16, const void* X, const void* W, int M, int N, int K, const Epilogue& e,
                  hipStream_t s);
 
+// ---------------------------------------------------------------- head + cross-entropy
+// Fused tied head for the loss (bf16, M > 64, K % 64 == 0): logits of X [M, K]
+// against W [N, K] are reduced in the product's epilogue to per-row partial
+// log-sum-exp states part [M][head_lse_parts(N)] (float2: max, sum of
+// exp(logit - max)) and the target logit tgt[m]; no logits are stored.
+bool head_lse_fused(bool bf16, int M, int K);
+int head_lse_parts(int N);
+void launch_head_lse(const void* X, const void* W, int M, int N, int K, const int32_t* targets, void* part,
+                     float* tgt, hipStream_t s);
+// loss[m] = logsumexp - target logit, from the partial states (fused head) or
+// from full fp32 logits rows [M, N] (otherwise).  A target outside [0, N)
+// gives NaN and ORs 1 into *flags.
+void launch_loss_from_parts(const void* part, int nparts, const float* tgt, const int32_t* targets, int M,
+                            int N, float* loss, uint32_t* flags, hipStream_t s);
+void launch_loss_from_logits(const float* logits, const int32_t* targets, int M, int N, float* loss,
+                             uint32_t* flags, hipStream_t s);
+
 // ---------------------------------------------------------------- attention
 // Causal attention for T new queries per sequence at positions l_past .. l_past+T-1
 // against keys 0 .. l_past+T-1 from the K/V view; q [B, h, T, d_h];

@@ -20,7 +20,8 @@ FP32, BF16 = 0, 1
 STATUS = {0: "GPT2_OK", 1: "GPT2_E_NULL", 2: "GPT2_E_SHAPE", 3: "GPT2_E_DTYPE",
           4: "GPT2_E_POSITION", 5: "GPT2_E_WORKSPACE", 6: "GPT2_E_TOKEN", 7: "GPT2_E_HIP"}
 EXPORTS = ("gpt2_workspace_size", "gpt2_block_forward", "gpt2_forward", "gpt2_prefill", "gpt2_decode_step",
-           "gpt2_generate_workspace_size", "gpt2_generate_greedy", "gpt2_read_device_flags",
+           "gpt2_generate_workspace_size", "gpt2_generate_greedy", "gpt2_loss_workspace_size",
+           "gpt2_forward_loss", "gpt2_read_device_flags",
            "gpt2_timing_begin", "gpt2_timing_end", "gpt2_status_str")
 BLOCK_KEYS = ("ln1_g", "ln1_b", "attn_w", "attn_b", "proj_w", "proj_b",
               "ln2_g", "ln2_b", "fc_w", "fc_b", "fc2_w", "fc2_b")
@@ -81,6 +82,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gpt2_generate_workspace_size.restype = sz
     lib.gpt2_generate_greedy.argtypes = [hp_p, ctypes.c_int, ctypes.POINTER(Weights), vp, i32, i32, i32,
                                          ctypes.POINTER(KV), vp, vp, sz, vp]
+    lib.gpt2_loss_workspace_size.argtypes = [hp_p, ctypes.c_int, i32, i32]
+    lib.gpt2_loss_workspace_size.restype = sz
+    lib.gpt2_forward_loss.argtypes = [hp_p, ctypes.c_int, ctypes.POINTER(Weights), vp, vp, i32, i32, vp,
+                                      ctypes.POINTER(KV), vp, sz, vp]
     lib.gpt2_read_device_flags.argtypes = [vp, vp]
     lib.gpt2_timing_begin.argtypes = []
     lib.gpt2_timing_begin.restype = ctypes.c_int
@@ -89,7 +94,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gpt2_status_str.argtypes = [ctypes.c_int]
     lib.gpt2_status_str.restype = ctypes.c_char_p
     for f in ("gpt2_block_forward", "gpt2_forward", "gpt2_prefill", "gpt2_decode_step", "gpt2_generate_greedy",
-              "gpt2_read_device_flags"):
+              "gpt2_forward_loss", "gpt2_read_device_flags"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -217,6 +222,25 @@ def generate_greedy(hp: HParams, mode: int, W: ModelWeights, ids, B: int, l_past
     _check(load().gpt2_generate_greedy(ctypes.byref(hp), mode, ctypes.byref(W.struct), _ptr(ids), B, l_past,
                                        n_new, ctypes.byref(kv), _ptr(out), _ptr(ws), ws_bytes, _stream(stream)),
            "gpt2_generate_greedy")
+
+
+def loss_workspace(hp: HParams, mode: int, B: int, T: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for forward_loss (uint8 tensor)."""
+    n = int(load().gpt2_loss_workspace_size(ctypes.byref(hp), mode, B, T))
+    if n == 0:
+        raise Gpt2Error(2, "gpt2_loss_workspace_size")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def forward_loss(hp: HParams, mode: int, W: ModelWeights, ids, targets, B: int, T: int, loss, present=None,
+                 capacity: int | None = None, ws=None, stream=None, ws_bytes=None):
+    ws_bytes = ws.numel() if ws_bytes is None and ws is not None else (ws_bytes or 0)
+    kv = None
+    if present is not None:
+        kv = KV(_ptr(present), capacity if capacity is not None else T)
+    _check(load().gpt2_forward_loss(ctypes.byref(hp), mode, ctypes.byref(W.struct), _ptr(ids), _ptr(targets), B, T,
+                                    _ptr(loss), ctypes.byref(kv) if kv is not None else None, _ptr(ws),
+                                    ws_bytes, _stream(stream)), "gpt2_forward_loss")
 
 
 def read_device_flags(ws, stream=None) -> int:

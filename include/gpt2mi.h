@@ -159,6 +159,25 @@ gpt2_status gpt2_generate_greedy(const gpt2_hparams *hp, gpt2_mode mode, const g
                                  const int32_t *ids, int32_t B, int32_t l_past, int32_t n_new,
                                  const gpt2_kv *cache, int32_t *out, void *ws, size_t ws_bytes, void *stream);
 
+/* Bytes of workspace gpt2_forward_loss needs (0 on bad arguments); zero-filled
+ * once before first use, like the others. */
+size_t gpt2_loss_workspace_size(const gpt2_hparams *hp, gpt2_mode mode, int32_t B, int32_t T);
+
+/* The uncached forward followed by the next-token cross-entropy that callers
+ * take of the logits ("Full Forward Pass", How it works): for ids [B, T] and
+ * targets [B, T] int32 (device; the token each position should predict, e.g.
+ * ids shifted by one), loss [B, T] fp32 (device) receives
+ * log(sum_n exp(logit_n)) - logit_target for every position.  The logits are
+ * not returned: in bf16 mode the head's epilogue keeps only per-row
+ * log-sum-exp partials (the 4 B x n_vocab per token logits never reach
+ * memory).  present as in gpt2_forward.  A target outside [0, n_vocab) gives a
+ * NaN loss and raises the same sticky flag as a bad token id
+ * (gpt2_read_device_flags).  Requires 1 <= T <= n_ctx and ws_bytes >=
+ * gpt2_loss_workspace_size(hp, mode, B, T). */
+gpt2_status gpt2_forward_loss(const gpt2_hparams *hp, gpt2_mode mode, const gpt2_weights *W,
+                              const int32_t *ids, const int32_t *targets, int32_t B, int32_t T, float *loss,
+                              const gpt2_kv *present, void *ws, size_t ws_bytes, void *stream);
+
 /* Synchronises `stream`, then reads and clears the workspace's sticky device
  * flags: GPT2_E_TOKEN if any earlier call on this workspace saw a token id
  * outside [0, n_vocab), else GPT2_OK (or GPT2_E_HIP). */

@@ -220,3 +220,15 @@ def decode_step(ids, W: dict, n_head: int, past, eps: float = EPS):
     [B, L, 2, h, 1, d_h])."""
     ids = np.asarray(ids).reshape(-1, 1)
     return model_forward(ids, W, n_head, past=past, eps=eps)
+
+
+def next_token_loss(logits, targets):
+    """Next-token cross-entropy that callers take of the logits ("Full Forward
+    Pass", How it works): per position, log(sum_n exp(logit_n)) -
+    logit_target, the log-sum-exp taken about the row maximum.
+    logits [..., V]; targets [...] ints in [0, V).  Returns [...] float64."""
+    z = _f64(logits)
+    t = np.asarray(targets)
+    mx = z.max(axis=-1, keepdims=True)
+    lse = mx[..., 0] + np.log(np.exp(z - mx).sum(axis=-1))
+    return lse - np.take_along_axis(z, t[..., None], axis=-1)[..., 0]

@@ -366,4 +366,29 @@ def pin_bruteforce_tiny():
         assert np.allclose(y, ref, rtol=0, atol=1e-12)
 
 
+def pin_loss_closed_forms():
+    # equal logits: every token has probability 1/V
+    V = 37
+    z = np.full((2, 3, V), 1.75)
+    t = np.array([[0, 5, 36], [1, 2, 3]])
+    assert np.allclose(O.next_token_loss(z, t), math.log(V), atol=1e-12)
+    # two classes: -log sigmoid(a - b) = log(1 + e^(b - a)) for target 0
+    a, b = 0.3, -1.9
+    got = O.next_token_loss(np.array([[a, b]]), np.array([0]))[0]
+    assert abs(got - math.log1p(math.exp(b - a))) < 1e-12
+    got = O.next_token_loss(np.array([[a, b]]), np.array([1]))[0]
+    assert abs(got - math.log1p(math.exp(a - b))) < 1e-12
+    # large logits: the max-subtracted form stays finite
+    got = O.next_token_loss(np.array([[1000.0, 0.0]]), np.array([1]))[0]
+    assert abs(got - 1000.0) < 1e-9
+
+
+def pin_loss_vs_torch():
+    rng = np.random.default_rng(7)
+    z = rng.normal(0, 3, (5, 11, 301))
+    t = rng.integers(0, 301, (5, 11))
+    ref = F.cross_entropy(_t(z).reshape(-1, 301), torch.tensor(t.reshape(-1)), reduction="none")
+    assert np.allclose(O.next_token_loss(z, t).reshape(-1), ref.numpy(), atol=1e-12)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -145,20 +145,26 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
     const uint4* vs = ks + 512;
     const int key0 = kb * 64;
     if (key0 <= wave_last) {
-      // ---- S^T for 2 x 32 keys
+      // ---- S^T for 2 x 32 keys: all eight K fragments read first, then the
+      // two independent accumulation chains interleaved
       f32x16_t s[2];
+      bf16x8_t kfr[2][4];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kk][r] = 0.f;
         const int row = kk * 32 + key_perm(l32);
 #pragma unroll
         for (int ds = 0; ds < 4; ++ds) {
           const int chunk = 2 * ds + kh;
-          const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, ks[row * 8 + (chunk ^ ((row >> 1) & 7))]);
-          s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kk], 0, 0, 0);
+          kfr[kk][ds] = __builtin_bit_cast(bf16x8_t, ks[row * 8 + (chunk ^ ((row >> 1) & 7))]);
         }
       }
+      const f32x16_t zero = {};
+      __builtin_amdgcn_sched_barrier(0);  // keep the eight reads ahead of the MFMAs
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[kk][ds], qf[ds], ds == 0 ? zero : s[kk], 0, 0, 0);
       // ---- mask (diagonal tiles only) and online softmax; register r of block
       // kk holds key key0 + 32*kk + 16*(r/8) + 8*kh + r%8.  The reference max
       // mref only moves when the tile max exceeds it by more than 8 (log2
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
       }
-      float ls = 0.f;
+      float ls4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
       bf16x8_t pf[4];  // 16-key P*V steps
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           p[r] = __builtin_amdgcn_exp2f(fmaf(s[kk][r], sc, -mrun));
-          ls += p[r];
+          ls4[r & 3] += p[r];
         }
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
@@ -205,7 +211,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
                                    pack_bf2(pp[6], pp[7])));
         }
       }
-      lrun += ls;
+      lrun += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
       // ---- O^T += V^T P^T over 4 steps of 16 keys (transposing reads of V)
       const char* vbytes = reinterpret_cast<const char*>(vs);
 #pragma unroll

@@ -7,7 +7,7 @@
 //
 // Three kernels:
 //  * attn_prefill_bf16: flash-style, 128 queries per workgroup (32 per wave),
-//    64-key K and V^T tiles moved to LDS by DMA through a 4-deep ring, online
+//    64-key K and V^T tiles moved to LDS by DMA through a 2-stage ring, online
 //    softmax in fp32 with exp2, MFMA 32x32x16 bf16 for Q K^T and P V.  Key tiles past the
 //    causal frontier are never loaded; tiles entirely above a wave's queries
 //    are skipped by that wave; only diagonal tiles apply the mask.
@@ -42,7 +42,9 @@ static constexpr float kLog2e = 1.4426950408889634f;
 // reads give a lane its 8 consecutive keys of one dim.  16-byte chunks are
 // XOR-swizzled per row: K by (key>>1)&7 (conflict-free 16-row fragment reads),
 // V by 4*((key>>1)&1) (conflict-free 4-row x 32-dim transposing reads).
-constexpr int kAttnStages = 4;
+// Two stages (32 KB) rather than four: three workgroups share a CU instead of
+// two, which measured faster (26.5 against 28.5 us per layer at B8 T1024).
+constexpr int kAttnStages = 2;
 constexpr int kAttnStageU4 = 2 * 64 * 8;  // K tile + V^T tile, uint4 units
 
 GPT2_DEV int key_perm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
                                                                 KvView kv, bf16_t* __restrict__ o,
                                                                 int H, int T, int l_past, int nqb) {
   constexpr int D = 64;
-  __shared__ uint4 lds[kAttnStages * kAttnStageU4];  // 64 KB
+  __shared__ uint4 lds[kAttnStages * kAttnStageU4];  // 16 KB per stage
 
   const int qb = nqb - 1 - (int)blockIdx.y;  // longest rows first
   const int bh = blockIdx.x;

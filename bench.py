@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the chunked-prefill, loss and generation measurements")
     return ap.parse_args()
 
 
@@ -166,8 +168,9 @@ def main():
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ chunked prefill, loss
-    result["prefill_chunk"] = bench_prefill_chunk(args, G, R, wl, Wd, hp, ids, stream, dev)
-    result["forward_loss"] = bench_forward_loss(args, G, R, wl, Wd, hp, ids, stream, dev)
+    if not args.no_extras:
+        result["prefill_chunk"] = bench_prefill_chunk(args, G, R, wl, Wd, hp, ids, stream, dev)
+        result["forward_loss"] = bench_forward_loss(args, G, R, wl, Wd, hp, ids, stream, dev)
 
     # ------------------------------------------------------------ decode workload
     if not args.no_decode:
@@ -316,6 +319,22 @@ def bench_decode(args, G, R, synth, wl, Wd, hp, stream, dev):
     avg_s = tot / n / 1e3
     ach = b / avg_s / 1e9
 
+    result = {
+        "value": round(wl.B / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+        "steps": args.decode_steps, "launch": "hip graph replay of one decode step",
+        "ms_per_step_eager": round(ms_eager, 4),
+        "workload": "GPT-2 small cached decode, bf16, B=64, one new token at position 1023, "
+                    "past [64,12,2,12,1023,64] ~ N(0,1)",
+        "hbm_frac_whole_step": round(byt / (ms / 1e3) / R.PEAK_HBM_BYTES, 4),
+        "algorithmic_bytes_per_step": byt,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": R.PEAK_HBM_BYTES / 1e9,
+                     "unit": "GB/s", "frac": round(ach * 1e9 / R.PEAK_HBM_BYTES, 4),
+                     "traffic": traffic_for("decode", dom), "work_per_launch": b, "avg_launch_us": round(avg_s * 1e6, 2)},
+        "kernels": kernels,
+    }
+    if args.no_extras:
+        return result
+
     # greedy generation: 32 tokens from position 991 on the same cache (the
     # loop rewrites slots 991..1022 with the same values on every run)
     n_new, start = 32, wl.l_past - 32
@@ -329,24 +348,11 @@ def bench_decode(args, G, R, synth, wl, Wd, hp, stream, dev):
     gen_ms = _timed_loop(gen, max(1, args.decode_steps // 10))
     log(f"[bench] greedy generation {n_new} tokens x {wl.B} sequences from position {start}: "
         f"{gen_ms:.3f} ms, {wl.B * n_new / (gen_ms / 1e3):.4g} tok/s")
-    generate = {"value": round(wl.B * n_new / (gen_ms / 1e3), 1), "unit": "tokens/s",
-                "ms_per_call": round(gen_ms, 4), "n_new": n_new, "from_position": start,
-                "workload": "GPT-2 small greedy generation (gpt2_generate_greedy), B=64, 32 tokens "
-                            "per sequence from position 991 over the decode workload's past"}
-    return {
-        "value": round(wl.B / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
-        "steps": args.decode_steps, "launch": "hip graph replay of one decode step",
-        "ms_per_step_eager": round(ms_eager, 4),
-        "workload": "GPT-2 small cached decode, bf16, B=64, one new token at position 1023, "
-                    "past [64,12,2,12,1023,64] ~ N(0,1)",
-        "hbm_frac_whole_step": round(byt / (ms / 1e3) / R.PEAK_HBM_BYTES, 4),
-        "algorithmic_bytes_per_step": byt,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": R.PEAK_HBM_BYTES / 1e9,
-                     "unit": "GB/s", "frac": round(ach * 1e9 / R.PEAK_HBM_BYTES, 4),
-                     "traffic": traffic_for("decode", dom), "work_per_launch": b, "avg_launch_us": round(avg_s * 1e6, 2)},
-        "kernels": kernels,
-        "generate": generate,
-    }
+    result["generate"] = {"value": round(wl.B * n_new / (gen_ms / 1e3), 1), "unit": "tokens/s",
+                          "ms_per_call": round(gen_ms, 4), "n_new": n_new, "from_position": start,
+                          "workload": "GPT-2 small greedy generation (gpt2_generate_greedy), B=64, 32 tokens "
+                                      "per sequence from position 991 over the decode workload's past"}
+    return result
 
 
 def cpu_baseline(wl, ids_np, W):

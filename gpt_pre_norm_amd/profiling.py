@@ -64,6 +64,8 @@ def kind_of(name: str, prev_kind: str | None) -> str:
         return "gemm_c_attn"
     if "EpiBiasGelu" in n:
         return "gemm_c_fc"
+    if "EpiLoss" in n:
+        return "gemm_lm_head_loss"
     if "EpiStoreF32" in n:
         return "gemm_lm_head"
     if "EpiResidInPlace" in n or "EpiBiasResid" in n:

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kk][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sc;
+      mx = halves_max(mx) * sc;
       if (mx > mrun + 8.0f) {
         const float alpha = __builtin_amdgcn_exp2f(mrun - mx);  // 0 on the first tile
         mrun = mx;
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
 
   // ---- normalise and store O [B, T, H*64]; lane holds query qw0 + l32 and
   // dims 32*db + 8*(r/4) + 4*kh + r%4
-  const float l = lrun + __shfl_xor(lrun, 32, 64);
+  const float l = halves_sum(lrun);
   const float inv = 1.0f / l;
   const int t = qw0 + l32;
   if (t < T) {
@@ -403,15 +403,17 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_bf16_kernel(const bf16_t*
       acc = fmaf(qv[5], bf_hi(u.z), acc);
       acc = fmaf(qv[6], bf_lo(u.w), acc);
       acc = fmaf(qv[7], bf_hi(u.w), acc);
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
-      acc += __shfl_xor(acc, 4, 64);
+      acc = sum8(acc);
       sv[i] = key0 + rg + 8 * i < nk ? acc * sc : -INFINITY;
       mx = fmaxf(mx, sv[i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 8, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    {  // max over the 8 row groups
+      float a, b;
+      mx = fmaxf(mx, dpp<kDppRor8>(mx));
+      row_pair<16>(mx, a, b);
+      row_pair<32>(fmaxf(a, b), a, b);
+      mx = fmaxf(a, b);
+    }
     const float mnew = fmaxf(m, mx);  // finite: key0 < nk, so row rg=0, i=0 is a real key
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
     m = mnew;
@@ -434,12 +436,16 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_bf16_kernel(const bf16_t*
     }
   }
   // sum the 8 row groups (each key's p is replicated over the 8 lanes of its row)
+  auto sum_groups = [](float v) {
+    float a, b;
+    v += dpp<kDppRor8>(v);
+    row_pair<16>(v, a, b);
+    row_pair<32>(a + b, a, b);
+    return a + b;
+  };
+  l = sum_groups(l);
 #pragma unroll
-  for (int off = 8; off < 64; off <<= 1) {
-    l += __shfl_xor(l, off, 64);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ov[e] += __shfl_xor(ov[e], off, 64);
-  }
+  for (int e = 0; e < 8; ++e) ov[e] = sum_groups(ov[e]);
   if (lane < 8) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) wo[wave][lane * 8 + e] = ov[e];

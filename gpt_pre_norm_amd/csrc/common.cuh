@@ -51,20 +51,117 @@ GPT2_DEV float4 load4(const bf16_t* p) {
   uint2 u = *reinterpret_cast<const uint2*>(p);
   return make_float4(bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y));
 }
+
+// Four elements as they come from memory, widened to fp32 only where they are
+// used: a load whose result is not touched right away does not stall the wave.
+template <typename T>
+struct Raw4;
+template <>
+struct Raw4<float> {
+  using type = float4;
+};
+template <>
+struct Raw4<bf16_t> {
+  using type = uint2;
+};
+GPT2_DEV float4 load4_raw(const float* p) { return *reinterpret_cast<const float4*>(p); }
+GPT2_DEV uint2 load4_raw(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+GPT2_DEV float4 widen4(float4 v) { return v; }
+GPT2_DEV float4 widen4(uint2 u) { return make_float4(bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y)); }
 GPT2_DEV void store4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 GPT2_DEV void store4(bf16_t* p, float4 v) {
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
 }
 
+// Cross-lane data movement without LDS. DPP (a VALU operand modifier) moves
+// values inside each row of 16 lanes; v_permlane16_swap / v_permlane32_swap
+// exchange whole rows / halves of the wave. A ds_bpermute-based shuffle
+// costs an LDS round trip per step instead.
+template <int CTRL>
+GPT2_DEV float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]: lane i <- i ^ 1
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]: lane i <- i ^ 2
+constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within each 8 lanes
+constexpr int kDppRor8 = 0x128;        // lane i <- i ^ 8 within each 16 lanes
+
+// Both orders of (lane's own row, partner row), for rows 16 apart (R = 16)
+// or halves 32 apart (R = 32): every lane receives {value of the even
+// row/half, value of the odd row/half}, so op(first, second) takes the same
+// operands in the same order in both partners.
+template <int R>
+GPT2_DEV void row_pair(float v, float& first, float& second) {
+  static_assert(R == 16 || R == 32, "row distance");
+  const unsigned u = __float_as_uint(v);
+  if constexpr (R == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    first = __uint_as_float(p[0]);
+    second = __uint_as_float(p[1]);
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    first = __uint_as_float(p[0]);
+    second = __uint_as_float(p[1]);
+  }
+}
+
+// op of a lane's value and the value 32 lanes away (the same in both lanes)
+template <typename Op>
+GPT2_DEV float halves(float v, Op op) {
+  float a, b;
+  row_pair<32>(v, a, b);
+  return op(a, b);
+}
+GPT2_DEV float halves_sum(float v) {
+  return halves(v, [](float x, float y) { return x + y; });
+}
+GPT2_DEV float halves_max(float v) {
+  return halves(v, [](float x, float y) { return fmaxf(x, y); });
+}
+
+// Sum of v over each group of 8 lanes, returned to all 8: two exact xor
+// steps, then the mirror within 8 lanes (exact here because all four lanes
+// of each quad already hold the same value).
+GPT2_DEV float sum8(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  return v + dpp<kDppHalfMirror>(v);
+}
+
+// Reduction over the 64 lanes with a commutative op, returned to every lane.
+template <typename Op>
+GPT2_DEV float wave_reduce(float v, Op op) {
+  v = op(v, dpp<kDppXor1>(v));
+  v = op(v, dpp<kDppXor2>(v));
+  v = op(v, dpp<kDppHalfMirror>(v));
+  v = op(v, dpp<kDppRor8>(v));
+  float a, b;
+  row_pair<16>(v, a, b);
+  v = op(a, b);
+  row_pair<32>(v, a, b);
+  return op(a, b);
+}
+// The same over a pair of values: op(x, y, x2, y2) folds state (x2, y2) into
+// (x, y). Integers travel as their bit patterns.
+template <typename Op>
+GPT2_DEV void wave_reduce2(float& x, float& y, Op op) {
+  op(x, y, dpp<kDppXor1>(x), dpp<kDppXor1>(y));
+  op(x, y, dpp<kDppXor2>(x), dpp<kDppXor2>(y));
+  op(x, y, dpp<kDppHalfMirror>(x), dpp<kDppHalfMirror>(y));
+  op(x, y, dpp<kDppRor8>(x), dpp<kDppRor8>(y));
+  float xb, yb;
+  row_pair<16>(x, x, xb);
+  row_pair<16>(y, y, yb);
+  op(x, y, xb, yb);
+  row_pair<32>(x, x, xb);
+  row_pair<32>(y, y, yb);
+  op(x, y, xb, yb);
+}
 GPT2_DEV float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return wave_reduce(v, [](float x, float y) { return x + y; });
 }
 GPT2_DEV float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
 
 // LayerNorm of one row by one wave ("GPT-2 Transformer block", norm()

@@ -115,9 +115,10 @@ struct EpiBiasGelu {
   const Tact* bias;
   Tact* out;
   int N;
-  using Ctx = float4;  // bias
-  GPT2_DEV Ctx load(int, int n) const { return load4(bias + n); }
-  GPT2_DEV void store(int m, int n, f32x4_t v, const Ctx& b) const {
+  using Ctx = typename Raw4<Tact>::type;  // bias
+  GPT2_DEV Ctx load(int, int n) const { return load4_raw(bias + n); }
+  GPT2_DEV void store(int m, int n, f32x4_t v, const Ctx& braw) const {
+    const float4 b = widen4(braw);
     store4(out + (long long)m * N + n,
            make_float4(gelu_tanh(v[0] + b.x), gelu_tanh(v[1] + b.y), gelu_tanh(v[2] + b.z),
                        gelu_tanh(v[3] + b.w)));
@@ -132,13 +133,14 @@ struct EpiBiasResid {
   Tout* out;
   int N;
   struct Ctx {
-    float4 b, r;  // bias, residual
+    typename Raw4<Tact>::type b;  // bias
+    typename Raw4<Tres>::type r;  // residual
   };
-  GPT2_DEV Ctx load(int m, int n) const { return {load4(bias + n), load4(res + (long long)m * N + n)}; }
+  GPT2_DEV Ctx load(int m, int n) const { return {load4_raw(bias + n), load4_raw(res + (long long)m * N + n)}; }
   GPT2_DEV void store(int m, int n, f32x4_t v, const Ctx& c) const {
+    const float4 b = widen4(c.b), r = widen4(c.r);
     store4(out + (long long)m * N + n,
-           make_float4(c.r.x + (v[0] + c.b.x), c.r.y + (v[1] + c.b.y), c.r.z + (v[2] + c.b.z),
-                       c.r.w + (v[3] + c.b.w)));
+           make_float4(r.x + (v[0] + b.x), r.y + (v[1] + b.y), r.z + (v[2] + b.z), r.w + (v[3] + b.w)));
   }
   GPT2_DEV void operator()(int m, int n, f32x4_t v) const { store(m, n, v, load(m, n)); }
 };
@@ -153,15 +155,16 @@ struct EpiResidInPlace {
   float* x;
   int N;
   struct Ctx {
-    float4 b, r;  // bias, residual
+    typename Raw4<Tact>::type b;  // bias
+    float4 r;                     // residual
   };
   GPT2_DEV Ctx load(int m, int n) const {
-    return {load4(bias + n), *reinterpret_cast<const float4*>(x + (long long)m * N + n)};
+    return {load4_raw(bias + n), *reinterpret_cast<const float4*>(x + (long long)m * N + n)};
   }
   GPT2_DEV void store(int m, int n, f32x4_t v, const Ctx& c) const {
+    const float4 b = widen4(c.b);
     *reinterpret_cast<float4*>(x + (long long)m * N + n) =
-        make_float4(c.r.x + (v[0] + c.b.x), c.r.y + (v[1] + c.b.y), c.r.z + (v[2] + c.b.z),
-                    c.r.w + (v[3] + c.b.w));
+        make_float4(c.r.x + (v[0] + b.x), c.r.y + (v[1] + b.y), c.r.z + (v[2] + b.z), c.r.w + (v[3] + b.w));
   }
   GPT2_DEV void operator()(int m, int n, f32x4_t v) const { store(m, n, v, load(m, n)); }
   GPT2_DEV void add(int m, int n, f32x4_t v, bool with_bias) const {
@@ -182,10 +185,11 @@ struct EpiQKV {
   KvView kv;
   int T, l_past, H, dh, d;
   FastDiv divT, divDh;
-  using Ctx = float4;  // bias
-  GPT2_DEV Ctx load(int, int n) const { return load4(bias + n); }
+  using Ctx = typename Raw4<Tact>::type;  // bias
+  GPT2_DEV Ctx load(int, int n) const { return load4_raw(bias + n); }
   GPT2_DEV void operator()(int m, int n, f32x4_t v) const { store(m, n, v, load(m, n)); }
-  GPT2_DEV void store(int m, int n, f32x4_t v, const Ctx& b) const {
+  GPT2_DEV void store(int m, int n, f32x4_t v, const Ctx& braw) const {
+    const float4 b = widen4(braw);
     const float4 y = make_float4(v[0] + b.x, v[1] + b.y, v[2] + b.z, v[3] + b.w);
     const int sec = (n >= d) + (n >= 2 * d);
     const int c = n - sec * d;
@@ -396,7 +400,7 @@ GPT2_DEV void lse_epilogue(const f32x16_t (&acc)[FN][FM], const EpiLoss& epi, in
         const int n = nw0 + a * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
         if (n < epi.N) mx = fmaxf(mx, acc[a][b][r]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = halves_max(mx);
     float sm = 0.f;
     const int t = m < M ? epi.targets[m] : -1;
 #pragma unroll
@@ -409,7 +413,7 @@ GPT2_DEV void lse_epilogue(const f32x16_t (&acc)[FN][FM], const EpiLoss& epi, in
           if (n == t) epi.tgt[m] = acc[a][b][r];
         }
       }
-    sm += __shfl_xor(sm, 32, 64);
+    sm = halves_sum(sm);
     if (kh == 0 && m < M) epi.part[(long long)m * epi.nparts + slot] = make_float2(mx, sm);
   }
   (void)WN;
@@ -419,6 +423,14 @@ template <class Epi>
 constexpr bool row_store() {
   if constexpr (requires { Epi::kRowStore; }) return Epi::kRowStore;
   else return false;
+}
+
+// Whether the epilogue's global reads are issued ahead of the last K stage
+// (all at once) or fragment by fragment inside the epilogue.
+template <class Epi>
+constexpr bool hoist_ctx() {
+  if constexpr (requires { Epi::kHoistCtx; }) return Epi::kHoistCtx;
+  else return true;
 }
 
 template <int N>
@@ -457,9 +469,32 @@ GPT2_DEV void wait_stage(int ahead) {
 // its own LDS patch as [m][n] (row pitch 36 floats) and reads it back with 8
 // lanes per row, so every epilogue access covers 8 rows x 32 consecutive columns.
 // (mw0, nw0) is the wave tile's first output row and column.
+// The epilogue's own global reads (bias, residual) for every element the lane
+// will store, issued in one batch before the last K stage's MFMAs so that
+// their latency is paid once and overlaps the tail of the main loop.
 template <int FM, int FN, class Epi>
-GPT2_DEV void tile_epilogue(const f32x16_t (&acc)[FN][FM], uint4* lds, const Epi& epi, int M, int N,
-                            int mw0, int nw0, int wave, int lane) {
+GPT2_DEV void tile_epilogue_loads(typename Epi::Ctx (&cx)[FN][FM][4], const Epi& epi, int M, int N, int mw0,
+                                  int nw0, int lane) {
+  if constexpr (!row_store<Epi>()) {
+    const int er = lane >> 3, ec = (lane & 7) * 4;
+#pragma unroll
+    for (int a = 0; a < FN; ++a)
+#pragma unroll
+      for (int b = 0; b < FM; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // unconditional, so the loads issue back to back; lanes outside
+          // the output read element (0, 0) and never use it
+          const int m = mw0 + b * 32 + 8 * i + er, n = nw0 + a * 32 + ec;
+          const bool in = m < M && n < N;
+          cx[a][b][i] = epi.load(in ? m : 0, in ? n : 0);
+        }
+  }
+}
+
+template <int FM, int FN, class Epi>
+GPT2_DEV void tile_epilogue(const f32x16_t (&acc)[FN][FM], const typename Epi::Ctx (&cx)[FN][FM][4], uint4* lds,
+                            const Epi& epi, int M, int N, int mw0, int nw0, int wave, int lane) {
   const int r32 = lane & 31, khalf = lane >> 5;
   float* patch = reinterpret_cast<float*>(lds) + wave * (32 * 36);
   const int er = lane >> 3;        // row within an 8-row group
@@ -488,19 +523,11 @@ GPT2_DEV void tile_epilogue(const f32x16_t (&acc)[FN][FM], uint4* lds, const Epi
           const float4 t = *reinterpret_cast<const float4*>(patch + (8 * i + er) * 36 + ec);
           v[i] = f32x4_t{t.x, t.y, t.z, t.w};
         }
-        // the epilogue's own reads (bias, residual) for all four rows go out
-        // together, so their latency is paid once per fragment
         const int n = nw0 + a * 32 + ec;
-        typename Epi::Ctx cx[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = mw0 + b * 32 + 8 * i + er;
-          if (m < M && n < N) cx[i] = epi.load(m, n);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = mw0 + b * 32 + 8 * i + er;
-          if (m < M && n < N) epi.store(m, n, v[i], cx[i]);
+          if (m < M && n < N) epi.store(m, n, v[i], cx[a][b][i]);
         }
       }
     }
@@ -617,28 +644,40 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_v3_kernel(const bf16
 #pragma unroll
   for (int f = 0; f < FM + FN; ++f) ldone(0, lds, 0, f);
 
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = 0; kt + 1 < nk; ++kt) {
     const uint4* st = lds + (kt % STAGES) * C::STAGE_U4;
 #pragma unroll
     for (int ks = 0; ks < KS - 1; ++ks) step(ks & 1, st, ks + 1);
-    if (kt + 1 < nk) {
-      // own loads of stage kt+1 done (later stages may stay in flight), this
-      // wave's reads of stage kt done; after the barrier both hold for all waves
-      wait_stage<C::LOADS, STAGES - 2>(min(STAGES - 2, nk - 2 - kt));
-      lds_barrier();
-      if (kt + STAGES < nk) issue(kt + STAGES, kt % STAGES);
-    }
+    // own loads of stage kt+1 done (later stages may stay in flight), this
+    // wave's reads of stage kt done; after the barrier both hold for all waves
+    wait_stage<C::LOADS, STAGES - 2>(min(STAGES - 2, nk - 2 - kt));
+    lds_barrier();
+    if (kt + STAGES < nk) issue(kt + STAGES, kt % STAGES);
     __builtin_amdgcn_sched_barrier(0);
-    // last step; on the final K step the reads of the following stage fetch
-    // unused data from the ring (in bounds, never consumed)
     step(1, lds + ((kt + 1) % STAGES) * C::STAGE_U4, 0);
   }
+  // the last K stage: no main-loop loads are waited for from here on
+  typename Epi::Ctx cx[FN][FM][4];
+  if constexpr (!row_lse<Epi>() && hoist_ctx<Epi>())
+    tile_epilogue_loads<FM, FN>(cx, epi, M, N, m0 + wm * WM, n0 + wn * WN, lane);
+  if (nk > 0) {
+    const int kt = nk - 1;
+    const uint4* st = lds + (kt % STAGES) * C::STAGE_U4;
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) step(ks & 1, st, ks + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // its reads of the following stage fetch unused data from the ring (in
+    // bounds, never consumed)
+    step(1, lds + ((kt + 1) % STAGES) * C::STAGE_U4, 0);
+  }
+  if constexpr (!row_lse<Epi>() && !hoist_ctx<Epi>())
+    tile_epilogue_loads<FM, FN>(cx, epi, M, N, m0 + wm * WM, n0 + wn * WN, lane);
 
   if constexpr (row_lse<Epi>()) {
     lse_epilogue<FM, FN, WN>(acc, epi, M, m0 + wm * WM, n0 + wn * WN, tn_idx * WGN + wn, lane);
   } else {
     __syncthreads();  // all waves are done reading the K stages
-    tile_epilogue<FM, FN>(acc, lds, epi, M, N, m0 + wm * WM, n0 + wn * WN, wave, lane);
+    tile_epilogue<FM, FN>(acc, cx, lds, epi, M, N, m0 + wm * WM, n0 + wn * WN, wave, lane);
   }
 }
 

@@ -25,15 +25,14 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_rows_kernel(const float
     }
   }
   auto better = [](float v, int i, float w, int j) { return w > v || (w == v && j < i); };
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float w = __shfl_xor(best, o, 64);
-    const int j = __shfl_xor(bi, o, 64);
-    if (better(best, bi, w, j)) {
-      best = w;
-      bi = j;
+  float bits = __int_as_float(bi);
+  wave_reduce2(best, bits, [&](float& v, float& ib, float w, float jb) {
+    if (better(v, __float_as_int(ib), w, __float_as_int(jb))) {
+      v = w;
+      ib = jb;
     }
-  }
+  });
+  bi = __float_as_int(bits);
   __shared__ float sv[kArgmaxThreads / 64];
   __shared__ int si[kArgmaxThreads / 64];
   if (lane == 0) {

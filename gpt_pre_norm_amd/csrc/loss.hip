@@ -38,8 +38,7 @@ __global__ __launch_bounds__(64) void loss_parts_kernel(const float2* __restrict
     const float2 p = part[(long long)m * nparts + i];
     merge(mx, sm, p.x, p.y);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) merge(mx, sm, __shfl_xor(mx, o, 64), __shfl_xor(sm, o, 64));
+  wave_reduce2(mx, sm, merge);
   if (lane == 0) {
     const int t = targets[m];
     loss[m] = finish(mx, sm, t >= 0 && t < N ? tgt[m] : 0.f, t, N, flags);
@@ -54,8 +53,7 @@ __global__ __launch_bounds__(256) void loss_logits_kernel(const float* __restric
   const float* row = logits + (long long)m * N;
   float mx = -INFINITY, sm = 0.f;
   for (int n = tid; n < N; n += 256) merge(mx, sm, row[n], 1.f);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) merge(mx, sm, __shfl_xor(mx, o, 64), __shfl_xor(sm, o, 64));
+  wave_reduce2(mx, sm, merge);
   __shared__ float wm[4], ws[4];
   if (lane == 0) {
     wm[wave] = mx;

@@ -7,7 +7,8 @@
 // fragments want; the W tile is the MFMA A operand and the X tile the B
 // operand, so each lane's accumulators hold consecutive output columns of one
 // row.  bf16 kernels, by shape:
-//   * M > 64, K % 64 == 0: 128x192 tiles (the head: 256x256), 8 waves of
+//   * M > 64, K % 64 == 0: 128x192 tiles (the head: 256x256 when M / 32 is a
+//     multiple of 256), 8 waves of
 //     v_mfma_f32_32x32x16_bf16, tiles DMA'd global -> LDS with
 //     global_load_lds_dwordx4 through a two-stage ring, epilogue through a
 //     per-wave LDS patch so stores cover whole rows of 128 bytes;
@@ -82,14 +83,17 @@ struct EpiStoreF32Lines {
   struct Ctx {};
   GPT2_DEV Ctx load(int, int) const { return {}; }
   GPT2_DEV void store(int i, int n, f32x4_t v, Ctx) const { (*this)(i, n, v); }
+  // Non-temporal stores: the logits are not read back by this kernel, and
+  // kept out of the way in L2 they leave it to the X and W tiles that every
+  // workgroup re-reads.
   GPT2_DEV void operator()(int i, int n, f32x4_t v) const {
     float* p = out + (long long)row_of(i) * N + n;
     if (n >= 0 && n + 3 < N) {
-      *reinterpret_cast<f32x4u_t*>(p) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4u_t*>(p));
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (n + r >= 0 && n + r < N) p[r] = v[r];
+        if (n + r >= 0 && n + r < N) __builtin_nontemporal_store(v[r], p + r);
     }
   }
 };
@@ -371,7 +375,7 @@ struct V2Cfg {
 
 template <class Epi>
 constexpr bool line_aligned() {
-  return std::is_same_v<Epi, EpiStoreF32Lines>;
+  return std::is_base_of_v<EpiStoreF32Lines, Epi>;
 }
 
 template <class Epi>
@@ -853,10 +857,16 @@ static void dispatch_bf16(const bf16_t* X, const bf16_t* W, int M, int N, int K,
     if (try_skinny(X, W, M, N, K, epi, s)) return;
     run_bf16<64, 64>(X, W, M, N, K, epi, s);
   } else if (K % 64 == 0) {
-    if constexpr (std::is_same_v<Epi, EpiStoreF32>)
-      run_bf16_v3<256, 256, 64, 2, EpiStoreF32Lines, 4, 2>(X, W, M, N, K,
-                                                          EpiStoreF32Lines::make(epi.out, N, M), s);
-    else
+    if constexpr (std::is_same_v<Epi, EpiStoreF32>) {
+      // a tile's rows share one line phase only when it lies inside one
+      // phase class (M / 32 rows): 256-row tiles when the classes hold a
+      // multiple of 256 rows, 128-row tiles otherwise
+      const auto lines = EpiStoreF32Lines::make(epi.out, N, M);
+      if (M % 32 == 0 && (M / 32) % 256 == 0)
+        run_bf16_v3<256, 256, 64, 2, EpiStoreF32Lines, 4, 2>(X, W, M, N, K, lines, s);
+      else
+        run_bf16_v3<128, 192, 64, 2, EpiStoreF32Lines, 4, 2>(X, W, M, N, K, lines, s);
+    } else
       run_bf16_v3<128, 192, 64, 2, Epi, 4, 2>(X, W, M, N, K, epi, s);
   } else {
     run_bf16<128, 128>(X, W, M, N, K, epi, s);

@@ -172,6 +172,14 @@ GPT2_DEV float wave_max(float v) {
 template <int NV, typename Tact>
 GPT2_DEV void ln_row_regs(const float4 (&v)[NV], const Tact* __restrict__ g, const Tact* __restrict__ b,
                           Tact* __restrict__ yr, int d, float eps, int lane) {
+  // gain and bias first: their loads overlap the row's reductions
+  typename Raw4<Tact>::type graw[NV], braw[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = min((lane + 64 * i) * 4, d - 4);
+    graw[i] = load4_raw(g + c);
+    braw[i] = load4_raw(b + c);
+  }
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
@@ -191,7 +199,7 @@ GPT2_DEV void ln_row_regs(const float4 (&v)[NV], const Tact* __restrict__ g, con
   for (int i = 0; i < NV; ++i) {
     const int c = (lane + 64 * i) * 4;
     if (c < d) {
-      const float4 gg = load4(g + c), bb = load4(b + c);
+      const float4 gg = widen4(graw[i]), bb = widen4(braw[i]);
       store4(yr + c, make_float4((v[i].x - mean) * rstd * gg.x + bb.x, (v[i].y - mean) * rstd * gg.y + bb.y,
                                  (v[i].z - mean) * rstd * gg.z + bb.z, (v[i].w - mean) * rstd * gg.w + bb.w));
     }

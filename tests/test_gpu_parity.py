@@ -105,6 +105,9 @@ def _small_model(mode, V, n_ctx, d, h, L, seed):
     (G.FP32, 1001, 64, 64, 4, 2, 2, 37),
     (G.BF16, 1001, 256, 128, 2, 2, 2, 150),
     (G.BF16, 517, 64, 64, 1, 3, 3, 1),
+    # wider rows through the line-aligned head: d = 256 and 768, one partial row tile
+    (G.BF16, 2001, 128, 256, 4, 1, 2, 100),
+    (G.BF16, 777, 128, 768, 12, 1, 1, 100),
 ])
 def test_forward_small(mode, V, n_ctx, d, h, L, B, T):
     W, Wd, hp = _small_model(mode, V, n_ctx, d, h, L, 400 + T)

@@ -171,6 +171,9 @@ def main():
     if not args.no_extras:
         result["prefill_chunk"] = bench_prefill_chunk(args, G, R, wl, Wd, hp, ids, stream, dev)
         result["forward_loss"] = bench_forward_loss(args, G, R, wl, Wd, hp, ids, stream, dev)
+        result["block"] = bench_block(args, G, R, WORKLOADS["block_gpt2s_bf16"], stream, dev)
+        result["forward_l48_d1600"] = bench_wide_forward(args, G, R, WORKLOADS["gpt2_l48_d1600_fwd_b4_t1024"],
+                                                         model_inputs, stream, dev)
 
     # ------------------------------------------------------------ decode workload
     if not args.no_decode:
@@ -257,6 +260,69 @@ def bench_forward_loss(args, G, R, wl, Wd, hp, ids, stream, dev):
             "loss_rows_us": round(loss_us, 2),
             "workload": "GPT-2 small forward B=8 T=1024 with the tied head fused into the next-token "
                         "cross-entropy (gpt2_forward_loss); per-position losses, no logits written"}
+
+
+def bench_block(args, G, R, wl, stream, dev):
+    """One GPT-2-small block at full size through gpt2_block_forward (bf16,
+    B=8, T=1024, present written)."""
+    import torch
+    from gpt_pre_norm_amd.workloads import block_inputs
+
+    x_np, w = block_inputs(wl)
+    hp = G.hparams(n_vocab=1, n_ctx=wl.n_ctx, n_embd=wl.d, n_head=wl.h, n_layer=1)
+    wd = G.upload_block(w, G.BF16)
+    x = G.to_device(x_np, G.BF16)
+    y = torch.empty_like(x)
+    pres = torch.empty((wl.B, 2, wl.h, wl.T, wl.dh), dtype=torch.bfloat16, device=dev)
+    ws = G.workspace(hp, G.BF16, wl.B, wl.T)
+
+    def run():
+        G.block_forward(hp, G.BF16, wd, x, y, wl.B, wl.T, present=pres, ws=ws, stream=stream)
+
+    for _ in range(max(1, args.warmup)):
+        run()
+    ms = _timed_loop(run, 5 * args.steps)
+    flops = R.model_flops(wl.B, wl.T, wl.d, wl.h, 1, 0)
+    log(f"[bench] block B={wl.B} T={wl.T} d={wl.d}: {ms * 1e3:.1f} us, {wl.tokens / (ms / 1e3):.4g} tok/s, "
+        f"{flops / (ms / 1e3) / 1e12:.1f} TFLOP/s")
+    del x, y, pres, ws, wd
+    torch.cuda.empty_cache()
+    return {"value": round(wl.tokens / (ms / 1e3), 1), "unit": "tokens/s", "us_per_call": round(ms * 1e3, 2),
+            "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+            "mfma_peak_frac": round(flops / (ms / 1e3) / R.PEAK_BF16_FLOPS, 4),
+            "workload": "one GPT-2-small block (gpt2_block_forward), bf16, B=8 T=1024 d=768 h=12, "
+                        "present written"}
+
+
+def bench_wide_forward(args, G, R, wl, model_inputs, stream, dev):
+    """The widest published depth: L=48, d=1600, 25 heads, B=4, T=1024,
+    uncached forward with fp32 logits."""
+    import torch
+
+    log(f"[bench] generating {wl.name}")
+    ids_np, W = model_inputs(wl)
+    Wd = G.upload_model(W, G.BF16)
+    del W
+    hp = G.hparams(n_vocab=wl.n_vocab, n_ctx=wl.n_ctx, n_embd=wl.d, n_head=wl.h, n_layer=wl.L)
+    ids = torch.from_numpy(ids_np).to(dev)
+    logits = torch.empty((wl.B, wl.T, wl.n_vocab), dtype=torch.float32, device=dev)
+    ws = G.workspace(hp, G.BF16, wl.B, wl.T)
+
+    def run():
+        G.forward(hp, G.BF16, Wd, ids, wl.B, wl.T, logits, ws=ws, stream=stream)
+
+    for _ in range(max(1, args.warmup)):
+        run()
+    ms = _timed_loop(run, max(3, args.steps // 2))
+    flops = R.model_flops(wl.B, wl.T, wl.d, wl.h, wl.L, wl.n_vocab)
+    log(f"[bench] forward L={wl.L} d={wl.d} B={wl.B} T={wl.T}: {ms:.3f} ms/step, "
+        f"{wl.tokens / (ms / 1e3):.4g} tok/s, {flops / (ms / 1e3) / 1e12:.1f} TFLOP/s")
+    del logits, ws, Wd
+    torch.cuda.empty_cache()
+    return {"value": round(wl.tokens / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+            "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+            "mfma_peak_frac": round(flops / (ms / 1e3) / R.PEAK_BF16_FLOPS, 4),
+            "workload": "L=48 d=1600 h=25 uncached forward, bf16, B=4 T=1024, V=50257, fp32 logits"}
 
 
 def bench_decode(args, G, R, synth, wl, Wd, hp, stream, dev):

@@ -221,8 +221,8 @@ def block_weights(d: int, seed: int, layer: int = 0, *, std: float = 0.02,
                 w[k] = normal((n,), 0.02, seed, base + 4 + j)
         else:
             w[k] = (np.ones if k.endswith("_g") else np.zeros)((n,), dtype=np.float32)
-    if bf16:
-        w = {k: round_bf16(v) for k, v in w.items()}
+    if bf16:  # the matrices were drawn already rounded; round the vectors
+        w = {k: (v if k.endswith("_w") else round_bf16(v)) for k, v in w.items()}
     return {k: w[k] for k in BLOCK_KEYS}
 
 
@@ -242,8 +242,8 @@ def model_weights(n_vocab: int, n_ctx: int, d: int, n_layer: int, seed: int, *,
         lnf_g = np.ones((d,), np.float32)
         lnf_b = np.zeros((d,), np.float32)
     W = {"wte": wte, "wpe": wpe, "lnf_g": lnf_g, "lnf_b": lnf_b}
-    if bf16:
-        W = {k: round_bf16(v) for k, v in W.items()}
+    if bf16:  # wte and wpe were drawn already rounded
+        W = {k: (v if k in ("wte", "wpe") else round_bf16(v)) for k, v in W.items()}
     W["blocks"] = [block_weights(d, seed, l, resid_scale=resid_scale, affine=affine, bf16=bf16)
                    for l in range(n_layer)]
     return W

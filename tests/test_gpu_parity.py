@@ -152,6 +152,41 @@ def test_forward_gpt2s_full():
     assert tol >= 0.999
 
 
+def test_forward_l48_d1600_full():
+    """The widest published depth at full size (L=48, d=1600, 25 heads, B=4,
+    T=1024): the oracle recomputes the first 192 positions of sequence 0 and
+    the first 96 of sequence 3 (logits on sampled rows, cache slots in full);
+    positions past them are checked through causality: a run on the first 192
+    tokens reproduces the full run's rows bit for bit."""
+    wl = WORKLOADS["gpt2_l48_d1600_fwd_b4_t1024"]
+    ids, W = model_inputs(wl)
+    Wd = G.upload_model(W, wl.mode)
+    hp = hp_of(wl.n_vocab, wl.n_ctx, wl.d, wl.h, wl.L)
+    cache = new_cache(wl.mode, wl.B, wl.L, wl.h, wl.n_ctx, wl.dh)
+    log("forward L=48 d=1600 full size")
+    logits, st = run_forward(wl.mode, hp, Wd, ids, cache=cache, capacity=wl.n_ctx)
+    assert st == 0
+    rng = np.random.default_rng(1)
+    g_all, o_all = [], []
+    for b, P in ((0, 192), (3, 96)):
+        rows = np.unique(np.concatenate([[0, 1, P // 2, P - 1], rng.integers(0, P, 16)]))
+        ol, opres = O.model_forward(ids[b:b + 1, :P], W, wl.h, logit_rows=rows)
+        g = to_np(logits[b, torch.from_numpy(rows).cuda()])
+        check(f"logits[{b}] ({len(rows)} of the first {P} rows)", g, ol, wl.mode)
+        check(f"cache[{b}] slots [0, {P})", to_np(cache[b:b + 1, ..., :P, :]), opres, wl.mode)
+        g_all.append(g)
+        o_all.append(ol)
+    tol, raw = argmax_agreement(np.concatenate(g_all), np.concatenate(o_all))
+    log(f"  argmax agreement tolerant {tol:.4f} raw {raw:.4f}")
+    assert tol >= 0.999
+    P = 192
+    cache2 = new_cache(wl.mode, wl.B, wl.L, wl.h, P, wl.dh)
+    logits2, st = run_forward(wl.mode, hp, Wd, np.ascontiguousarray(ids[:, :P]), cache=cache2, capacity=P)
+    assert st == 0
+    assert torch.equal(logits2, logits[:, :P]), "a prefix run differs from the full run's rows"
+    assert torch.equal(cache2, cache[..., :P, :])
+
+
 @pytest.mark.parametrize("mode", [G.FP32, G.BF16])
 def test_forward_causality_bit_identical(mode):
     V, n_ctx, d, h, L, B, T = 300, 256, 128, 2, 2, 2, 200

@@ -14,7 +14,7 @@
 //  * attn_rows_f32: one wave per query row with a full (max-subtracted)
 //    softmax, for the fp32 mode.
 //  * attn_decode_bf16: one new query per (sequence, head) streaming the cache
-//    with one 16-wave workgroup per (sequence, head); the waves' online
+//    with one 4-wave workgroup per (sequence, head); the waves' online
 //    softmax states merge in LDS.
 #include "kernels.h"
 

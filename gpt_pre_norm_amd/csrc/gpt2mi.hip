@@ -171,9 +171,9 @@ void timed(int kind, hipStream_t s, F&& launch) {
     return;
   }
   hipEvent_t a = g_timing.take(), b = g_timing.take();
-  if (a) hipEventRecord(a, s);
+  if (a && hipEventRecord(a, s) != hipSuccess) g_timing.failed = true;
   launch();
-  if (b) hipEventRecord(b, s);
+  if (b && hipEventRecord(b, s) != hipSuccess) g_timing.failed = true;
   g_timing.kinds.push_back(kind);
 }
 

@@ -58,14 +58,27 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
 
 GPT2_DEV int v_swz(int key) { return ((key >> 1) & 1) << 2; }
 
+// Work items (head, query block) in order of decreasing length are dealt in
+// rounds of one per CU slot, every other round reversed, so that the CUs
+// that took the longest blocks of one round take the shortest of the next.
+GPT2_DEV void attn_item(int i, int nbh, int nqb, int round, int& bh, int& qb) {
+  const int total = nbh * nqb;
+  const int r = i / round, p = i - r * round;
+  const int chunk = min(round, total - r * round);
+  const int j = r * round + ((r & 1) ? chunk - 1 - p : p);
+  qb = nqb - 1 - j / nbh;
+  bh = j - (j / nbh) * nbh;
+}
+
 __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __restrict__ q,
                                                                 KvView kv, bf16_t* __restrict__ o,
-                                                                int H, int T, int l_past, int nqb) {
+                                                                int H, int T, int l_past, int nbh, int nqb,
+                                                                int round) {
   constexpr int D = 64;
   __shared__ uint4 lds[kAttnStages * kAttnStageU4];  // 16 KB per stage
 
-  const int qb = nqb - 1 - (int)blockIdx.y;  // longest rows first
-  const int bh = blockIdx.x;
+  int qb, bh;
+  attn_item(blockIdx.x, nbh, nqb, round, bh, qb);
   const int b = bh / H, h = bh - (bh / H) * H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, kh = lane >> 5;
@@ -255,8 +268,14 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
 void launch_attn_prefill_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int T, int l_past,
                               hipStream_t s) {
   const int nqb = (T + 127) / 128;
-  dim3 grid(B * H, nqb);
-  attn_prefill_bf16_kernel<<<grid, 256, 0, s>>>(q, kv, o, H, T, l_past, nqb);
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+      n_cu = 256;
+  }
+  attn_prefill_bf16_kernel<<<B * H * nqb, 256, 0, s>>>(q, kv, o, H, T, l_past, B * H, nqb, n_cu);
 }
 
 // ================================================================ row-wise (fp32)

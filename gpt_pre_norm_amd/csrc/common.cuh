@@ -223,11 +223,10 @@ GPT2_DEV void ln_row_wave(const Tin* __restrict__ xr, const Tact* __restrict__ g
 // x / (1 + 2^(-2u log2 e)), with the hardware exp2 and reciprocal (about 1 ulp
 // each).  Large |u| saturates correctly: exp2 -> inf gives 0, exp2 -> 0 gives x.
 GPT2_DEV float gelu_tanh(float x) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-  const float k1 = 0.044715f;
-  const float m2log2e = -2.0f * 1.4426950408889634f;
-  const float u = k0 * x * fmaf(k1, x * x, 1.0f);
-  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m2log2e * u));
+  // -2 u log2(e) = x (c1 + c2 x^2), c1 = -2 log2(e) sqrt(2/pi), c2 = 0.044715 c1
+  const float c1 = -2.0f * 1.4426950408889634f * 0.7978845608028654f;
+  const float c2 = 0.044715f * c1;
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * fmaf(c2, x * x, c1)));
 }
 
 // Unsigned division by a run-time constant d >= 1 with a precomputed

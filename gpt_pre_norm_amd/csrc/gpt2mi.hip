@@ -30,6 +30,10 @@ constexpr int kMaxRowKeysF32 = 8192;  // fp32 row-wise attention keeps a row of 
 
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// Workspace regions are carved at kAlign offsets from its start, so the start
+// itself must be kAlign-aligned (every hipMalloc / torch allocation is).
+bool ws_aligned(const void* ws) { return (uintptr_t)ws % kAlign == 0; }
+
 struct Layout {
   size_t x, a, q, o, u, kv, total;
 };
@@ -125,7 +129,7 @@ gpt2_status check_common(const gpt2_hparams& hp, gpt2_mode mode, int B, int T, i
   if (l_past < 0 || (long long)l_past + T > hp.n_ctx) return GPT2_E_POSITION;
   if (mode == GPT2_FP32 && l_past + T > kMaxRowKeysF32) return GPT2_E_SHAPE;
   if (!ws) return GPT2_E_NULL;
-  if (ws_bytes < layout(hp, mode, B, T).total) return GPT2_E_WORKSPACE;
+  if (!ws_aligned(ws) || ws_bytes < layout(hp, mode, B, T).total) return GPT2_E_WORKSPACE;
   return GPT2_OK;
 }
 
@@ -314,7 +318,7 @@ const char* gpt2_status_str(gpt2_status st) {
     case GPT2_E_SHAPE: return "unsupported or inconsistent sizes";
     case GPT2_E_DTYPE: return "unknown mode";
     case GPT2_E_POSITION: return "positions exceed n_ctx or the cache capacity";
-    case GPT2_E_WORKSPACE: return "workspace too small";
+    case GPT2_E_WORKSPACE: return "workspace too small or misaligned";
     case GPT2_E_TOKEN: return "token id outside [0, n_vocab)";
     case GPT2_E_HIP: return "HIP runtime error";
   }
@@ -414,7 +418,7 @@ gpt2_status gpt2_generate_greedy(const gpt2_hparams* hp, gpt2_mode mode, const g
     return GPT2_E_POSITION;
   if (mode == GPT2_FP32 && l_past + n_new > kMaxRowKeysF32) return GPT2_E_SHAPE;
   const GenLayout G = gen_layout(*hp, mode, B);
-  if (ws_bytes < G.total) return GPT2_E_WORKSPACE;
+  if (!ws_aligned(ws) || ws_bytes < G.total) return GPT2_E_WORKSPACE;
   (void)hipGetLastError();
   char* w = (char*)ws;
   float* logits = (float*)(w + G.logits);
@@ -445,7 +449,7 @@ gpt2_status gpt2_forward_loss(const gpt2_hparams* hp, gpt2_mode mode, const gpt2
   st = check_common(*hp, mode, B, T, 0, ws, 0);
   if (st != GPT2_OK && st != GPT2_E_WORKSPACE) return st;
   const LossLayout G = loss_layout(*hp, mode, B, T);
-  if (ws_bytes < G.total) return GPT2_E_WORKSPACE;
+  if (!ws_aligned(ws) || ws_bytes < G.total) return GPT2_E_WORKSPACE;
   if (present && present->capacity < T) return GPT2_E_POSITION;
   (void)hipGetLastError();
   Run r{*hp, mode, B, T, 0, false, (char*)ws, G.fwd, (hipStream_t)stream};

@@ -52,7 +52,7 @@ typedef enum {
   GPT2_E_SHAPE = 2,     /* unsupported or inconsistent sizes */
   GPT2_E_DTYPE = 3,     /* unknown mode */
   GPT2_E_POSITION = 4,  /* l_past + T exceeds n_ctx or the cache capacity */
-  GPT2_E_WORKSPACE = 5, /* ws_bytes smaller than gpt2_workspace_size() */
+  GPT2_E_WORKSPACE = 5, /* ws_bytes smaller than gpt2_workspace_size(), or ws misaligned */
   GPT2_E_TOKEN = 6,     /* a token id was outside [0, n_vocab) (device flag) */
   GPT2_E_HIP = 7        /* the HIP runtime reported an error */
 } gpt2_status;
@@ -96,7 +96,9 @@ typedef struct {
 /* Bytes of workspace any of the compute calls needs for batch B and T new
  * tokens per sequence (T = 1 for gpt2_decode_step).  0 on bad arguments.
  * A new workspace must be zero-filled once before its first use (the first
- * 256 bytes hold the sticky device flags). */
+ * 256 bytes hold the sticky device flags).  Every call takes the workspace
+ * start 256-byte aligned (as any hipMalloc or torch allocation is); a
+ * misaligned one gives GPT2_E_WORKSPACE. */
 size_t gpt2_workspace_size(const gpt2_hparams *hp, gpt2_mode mode, int32_t B, int32_t T);
 
 /* One pre-norm block ("Decoder Block", How it works) on x [B, T, d] -> y [B, T, d]

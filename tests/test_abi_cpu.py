@@ -54,7 +54,7 @@ def _block_weights():
 
 @pytest.mark.parametrize("case,expect", [
     ("bad_mode", 3), ("bad_heads", 2), ("null_x", 1), ("null_weight", 1), ("T_over_ctx", 4),
-    ("zero_B", 2), ("small_ws", 5), ("null_ws", 1)])
+    ("zero_B", 2), ("small_ws", 5), ("null_ws", 1), ("misaligned_ws", 5)])
 def test_block_forward_argument_errors(case, expect):
     lib = G.load()
     hp = G.hparams(n_ctx=16)
@@ -76,6 +76,8 @@ def test_block_forward_argument_errors(case, expect):
         nbytes = 1024
     elif case == "null_ws":
         ws = None
+    elif case == "misaligned_ws":
+        ws = FAKE + 16  # regions are carved at 256-byte offsets from the start
     st = lib.gpt2_block_forward(ctypes.byref(hp), mode, ctypes.byref(w), x, FAKE, B, T, None, ws, nbytes,
                                 None)
     assert st == expect, (st, G.STATUS.get(st))
@@ -138,9 +140,9 @@ def test_generate_argument_errors():
     small = G.KV(FAKE, 600)
     big = 1 << 40
 
-    def call(B, l_past, n_new, cache, out=FAKE, ws_bytes=big):
+    def call(B, l_past, n_new, cache, out=FAKE, ws_bytes=big, ws=FAKE):
         return lib.gpt2_generate_greedy(ctypes.byref(hp), G.BF16, ctypes.byref(W), FAKE, B, l_past, n_new,
-                                        ctypes.byref(cache) if cache is not None else None, out, FAKE,
+                                        ctypes.byref(cache) if cache is not None else None, out, ws,
                                         ws_bytes, None)
 
     assert call(2, 1000, 25, kv) == 4      # positions past n_ctx
@@ -151,5 +153,6 @@ def test_generate_argument_errors():
     assert call(2, 10, 5, None) == 1
     assert call(2, 10, 5, kv, out=None) == 1
     assert call(2, 10, 5, kv, ws_bytes=16) == 5
+    assert call(2, 10, 5, kv, ws=FAKE + 8) == 5
     need = G.load().gpt2_generate_workspace_size(ctypes.byref(hp), G.BF16, 2)
     assert need > G.workspace_size(hp, G.BF16, 2, 1)   # the step's regions plus logits and tokens

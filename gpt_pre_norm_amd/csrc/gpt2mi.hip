@@ -34,6 +34,12 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // itself must be kAlign-aligned (every hipMalloc / torch allocation is).
 bool ws_aligned(const void* ws) { return (uintptr_t)ws % kAlign == 0; }
 
+// Weights, activations and the cache are read with 16-byte vector and DMA
+// loads; ids, targets and fp32 outputs with 4-byte accesses.  NULL passes
+// (NULL checks are separate).
+bool al16(const void* p) { return (uintptr_t)p % 16 == 0; }
+bool al4(const void* p) { return (uintptr_t)p % 4 == 0; }
+
 struct Layout {
   size_t x, a, q, o, u, kv, total;
 };
@@ -116,10 +122,19 @@ bool any_null(const gpt2_block_weights& w) {
          !w.ln2_b || !w.fc_w || !w.fc_b || !w.fc2_w || !w.fc2_b;
 }
 
+bool all_al16(const gpt2_block_weights& w) {
+  return al16(w.ln1_g) && al16(w.ln1_b) && al16(w.attn_w) && al16(w.attn_b) && al16(w.proj_w) &&
+         al16(w.proj_b) && al16(w.ln2_g) && al16(w.ln2_b) && al16(w.fc_w) && al16(w.fc_b) && al16(w.fc2_w) &&
+         al16(w.fc2_b);
+}
+
 gpt2_status check_weights(const gpt2_hparams& hp, const gpt2_weights* W) {
   if (!W || !W->wte || !W->wpe || !W->lnf_g || !W->lnf_b || !W->blocks) return GPT2_E_NULL;
   for (int l = 0; l < hp.n_layer; ++l)
     if (any_null(W->blocks[l])) return GPT2_E_NULL;
+  if (!al16(W->wte) || !al16(W->wpe) || !al16(W->lnf_g) || !al16(W->lnf_b)) return GPT2_E_ALIGN;
+  for (int l = 0; l < hp.n_layer; ++l)
+    if (!all_al16(W->blocks[l])) return GPT2_E_ALIGN;
   return GPT2_OK;
 }
 
@@ -321,6 +336,7 @@ const char* gpt2_status_str(gpt2_status st) {
     case GPT2_E_WORKSPACE: return "workspace too small or misaligned";
     case GPT2_E_TOKEN: return "token id outside [0, n_vocab)";
     case GPT2_E_HIP: return "HIP runtime error";
+    case GPT2_E_ALIGN: return "a device pointer is misaligned";
   }
   return "unknown status";
 }
@@ -338,6 +354,7 @@ gpt2_status gpt2_block_forward(const gpt2_hparams* hp, gpt2_mode mode, const gpt
   if (st != GPT2_OK) return st;
   if (!w || !x || !y) return GPT2_E_NULL;
   if (any_null(*w)) return GPT2_E_NULL;
+  if (!all_al16(*w) || !al16(x) || !al16(y) || !al16(present)) return GPT2_E_ALIGN;
   st = check_common(*hp, mode, B, T, 0, ws, ws_bytes);
   if (st != GPT2_OK) return st;
   (void)hipGetLastError();
@@ -355,6 +372,7 @@ gpt2_status gpt2_forward(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_weig
   if (!ids || !logits) return GPT2_E_NULL;
   if ((st = check_weights(*hp, W)) != GPT2_OK) return st;
   if (present && !present->data) return GPT2_E_NULL;
+  if (!al4(ids) || !al4(logits) || (present && !al16(present->data))) return GPT2_E_ALIGN;
   st = check_common(*hp, mode, B, T, 0, ws, ws_bytes);
   if (st != GPT2_OK) return st;
   if (present && present->capacity < T) return GPT2_E_POSITION;
@@ -372,6 +390,7 @@ gpt2_status gpt2_decode_step(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_
   if (!ids || !logits || !cache) return GPT2_E_NULL;
   if (!cache->data) return GPT2_E_NULL;
   if ((st = check_weights(*hp, W)) != GPT2_OK) return st;
+  if (!al4(ids) || !al4(logits) || !al16(cache->data)) return GPT2_E_ALIGN;
   st = check_common(*hp, mode, B, 1, l_past, ws, ws_bytes);
   if (st != GPT2_OK) return st;
   if (l_past >= cache->capacity) return GPT2_E_POSITION;
@@ -389,6 +408,7 @@ gpt2_status gpt2_prefill(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_weig
   if (!ids || !logits || !cache) return GPT2_E_NULL;
   if (!cache->data) return GPT2_E_NULL;
   if ((st = check_weights(*hp, W)) != GPT2_OK) return st;
+  if (!al4(ids) || !al4(logits) || !al16(cache->data)) return GPT2_E_ALIGN;
   st = check_common(*hp, mode, B, T, l_past, ws, ws_bytes);
   if (st != GPT2_OK) return st;
   if ((long long)l_past + T > cache->capacity) return GPT2_E_POSITION;
@@ -413,6 +433,7 @@ gpt2_status gpt2_generate_greedy(const gpt2_hparams* hp, gpt2_mode mode, const g
   if (!ids || !out || !cache || !ws) return GPT2_E_NULL;
   if (!cache->data) return GPT2_E_NULL;
   if ((st = check_weights(*hp, W)) != GPT2_OK) return st;
+  if (!al4(ids) || !al4(out) || !al16(cache->data)) return GPT2_E_ALIGN;
   if (B < 1 || n_new < 1 || B > kMaxTokens) return GPT2_E_SHAPE;
   if (l_past < 0 || (long long)l_past + n_new > hp->n_ctx || (long long)l_past + n_new > cache->capacity)
     return GPT2_E_POSITION;
@@ -446,6 +467,7 @@ gpt2_status gpt2_forward_loss(const gpt2_hparams* hp, gpt2_mode mode, const gpt2
   if (!ids || !targets || !loss) return GPT2_E_NULL;
   if ((st = check_weights(*hp, W)) != GPT2_OK) return st;
   if (present && !present->data) return GPT2_E_NULL;
+  if (!al4(ids) || !al4(targets) || !al4(loss) || (present && !al16(present->data))) return GPT2_E_ALIGN;
   st = check_common(*hp, mode, B, T, 0, ws, 0);
   if (st != GPT2_OK && st != GPT2_E_WORKSPACE) return st;
   const LossLayout G = loss_layout(*hp, mode, B, T);

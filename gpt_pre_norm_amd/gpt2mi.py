@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(HERE, "libgpt2mi.so")
 
 FP32, BF16 = 0, 1
 STATUS = {0: "GPT2_OK", 1: "GPT2_E_NULL", 2: "GPT2_E_SHAPE", 3: "GPT2_E_DTYPE",
-          4: "GPT2_E_POSITION", 5: "GPT2_E_WORKSPACE", 6: "GPT2_E_TOKEN", 7: "GPT2_E_HIP"}
+          4: "GPT2_E_POSITION", 5: "GPT2_E_WORKSPACE", 6: "GPT2_E_TOKEN", 7: "GPT2_E_HIP",
+          8: "GPT2_E_ALIGN"}
 EXPORTS = ("gpt2_workspace_size", "gpt2_block_forward", "gpt2_forward", "gpt2_prefill", "gpt2_decode_step",
            "gpt2_generate_workspace_size", "gpt2_generate_greedy", "gpt2_loss_workspace_size",
            "gpt2_forward_loss", "gpt2_read_device_flags",

@@ -35,6 +35,11 @@
  *     embedding kernel zero-fills that row and raises a sticky device flag in
  *     the workspace that gpt2_read_device_flags reports and clears.
  *   - Concurrent calls must use distinct workspaces.
+ *   - Device pointers to weights, activations and the K/V cache must be
+ *     16-byte aligned; token ids, targets, outputs of ids and fp32 logits /
+ *     losses 4-byte aligned; the workspace 256-byte aligned (any hipMalloc or
+ *     torch allocation is).  A misaligned pointer gives GPT2_E_ALIGN
+ *     (GPT2_E_WORKSPACE for the workspace).
  */
 #ifndef GPT2MI_H
 #define GPT2MI_H
@@ -54,7 +59,8 @@ typedef enum {
   GPT2_E_POSITION = 4,  /* l_past + T exceeds n_ctx or the cache capacity */
   GPT2_E_WORKSPACE = 5, /* ws_bytes smaller than gpt2_workspace_size(), or ws misaligned */
   GPT2_E_TOKEN = 6,     /* a token id was outside [0, n_vocab) (device flag) */
-  GPT2_E_HIP = 7        /* the HIP runtime reported an error */
+  GPT2_E_HIP = 7,       /* the HIP runtime reported an error */
+  GPT2_E_ALIGN = 8      /* a device pointer is not aligned as the conventions require */
 } gpt2_status;
 
 typedef enum { GPT2_FP32 = 0, GPT2_BF16 = 1 } gpt2_mode;

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(8):
+    for st in range(9):
         assert G.status_str(st)
     assert G.status_str(6).startswith("token id")
 
@@ -54,7 +54,8 @@ def _block_weights():
 
 @pytest.mark.parametrize("case,expect", [
     ("bad_mode", 3), ("bad_heads", 2), ("null_x", 1), ("null_weight", 1), ("T_over_ctx", 4),
-    ("zero_B", 2), ("small_ws", 5), ("null_ws", 1), ("misaligned_ws", 5)])
+    ("zero_B", 2), ("small_ws", 5), ("null_ws", 1), ("misaligned_ws", 5), ("misaligned_x", 8),
+    ("misaligned_weight", 8)])
 def test_block_forward_argument_errors(case, expect):
     lib = G.load()
     hp = G.hparams(n_ctx=16)
@@ -78,6 +79,10 @@ def test_block_forward_argument_errors(case, expect):
         ws = None
     elif case == "misaligned_ws":
         ws = FAKE + 16  # regions are carved at 256-byte offsets from the start
+    elif case == "misaligned_x":
+        x = FAKE + 8    # rows are read with 16-byte vector loads
+    elif case == "misaligned_weight":
+        w.attn_w = FAKE + 2
     st = lib.gpt2_block_forward(ctypes.byref(hp), mode, ctypes.byref(w), x, FAKE, B, T, None, ws, nbytes,
                                 None)
     assert st == expect, (st, G.STATUS.get(st))
@@ -104,6 +109,11 @@ def test_decode_and_forward_position_errors():
                             FAKE, big, None) == 4
     assert lib.gpt2_decode_step(ctypes.byref(hp), G.BF16, ctypes.byref(W), FAKE, 4, 5, None, FAKE, FAKE, big,
                                 None) == 1
+    assert lib.gpt2_forward(ctypes.byref(hp), G.BF16, ctypes.byref(W), FAKE + 1, 2, 4, FAKE, None, FAKE, big,
+                            None) == 8   # ids must be 4-byte aligned
+    Wm = G.Weights(FAKE + 4, FAKE, FAKE, FAKE, ctypes.cast(blocks, ctypes.POINTER(G.BlockWeights)))
+    assert lib.gpt2_decode_step(ctypes.byref(hp), G.BF16, ctypes.byref(Wm), FAKE, 4, 5, ctypes.byref(kv),
+                                FAKE, FAKE, big, None) == 8   # wte must be 16-byte aligned
     hp0 = G.hparams(n_vocab=0)
     assert lib.gpt2_forward(ctypes.byref(hp0), G.BF16, ctypes.byref(W), FAKE, 2, 4, FAKE, None, FAKE, big,
                             None) == 2
@@ -129,6 +139,7 @@ def test_prefill_argument_errors():
     assert call(2, 0, 10, kv) == 2
     assert call(2, 10, 10, None) == 1
     assert call(2, 10, 10, kv, ws_bytes=16) == 5
+    assert call(2, 10, 10, G.KV(FAKE + 8, 1024)) == 8
 
 
 def test_generate_argument_errors():
@@ -154,5 +165,7 @@ def test_generate_argument_errors():
     assert call(2, 10, 5, kv, out=None) == 1
     assert call(2, 10, 5, kv, ws_bytes=16) == 5
     assert call(2, 10, 5, kv, ws=FAKE + 8) == 5
+    assert call(2, 10, 5, kv, out=FAKE + 2) == 8
+    assert call(2, 10, 5, G.KV(FAKE + 4, 1024)) == 8
     need = G.load().gpt2_generate_workspace_size(ctypes.byref(hp), G.BF16, 2)
     assert need > G.workspace_size(hp, G.BF16, 2, 1)   # the step's regions plus logits and tokens

@@ -808,11 +808,19 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16_t* __restri
 }
 
 // K ranges for the skinny kernel: the fewest that keep kc = K/S <= 768 with
-// K/S a multiple of 128 (16 chunks per LDS row).  0 if none exists.
-static int skinny_splits(int K) {
+// K/S a multiple of 128 (16 chunks per LDS row) and, where the epilogue can
+// take K ranges (min_wg > 0), give at least min_wg workgroups over the
+// nslices column slices.  Each range adds its M x N fp32 atomics, so no more
+// than that: at M = 64, N = K = 768 (48 slices) two ranges took 4.5 us
+// against 5.3 us for one and 6.7 us for six.  0 if none exists.
+static int skinny_splits(int K, int nslices = 0, int min_wg = 0) {
+  int first = 0;
   for (int s = 1; s <= K / 128; ++s)
-    if (K % s == 0 && (K / s) % 128 == 0 && K / s <= kSkinnyMaxKc) return s;
-  return 0;
+    if (K % s == 0 && (K / s) % 128 == 0 && K / s <= kSkinnyMaxKc) {
+      if (!first) first = s;
+      if (nslices * s >= min_wg) return s;
+    }
+  return first;
 }
 
 template <int NT, class Epi>
@@ -835,7 +843,8 @@ template <class Epi>
 static bool try_skinny(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
                        hipStream_t s) {
   if (M > 64) return false;
-  const int S = skinny_splits(K);
+  const int nslices = N >= 8192 ? (N + 31) / 32 : (N + 15) / 16;
+  const int S = atomic_resid<Epi>() ? skinny_splits(K, nslices, 96) : skinny_splits(K);
   if (S == 0 || (S > 1 && !atomic_resid<Epi>())) return false;
   if (N >= 8192)
     run_skinny<32>(X, W, M, N, K, S, epi, s);

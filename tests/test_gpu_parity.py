@@ -108,6 +108,8 @@ def _small_model(mode, V, n_ctx, d, h, L, seed):
     # wider rows through the line-aligned head: d = 256 and 768, one partial row tile
     (G.BF16, 2001, 128, 256, 4, 1, 2, 100),
     (G.BF16, 777, 128, 768, 12, 1, 1, 100),
+    # 60 rows: the skinny products with the LayerNorm in their prologue
+    (G.BF16, 2001, 128, 256, 4, 1, 2, 30),
 ])
 def test_forward_small(mode, V, n_ctx, d, h, L, B, T):
     W, Wd, hp = _small_model(mode, V, n_ctx, d, h, L, 400 + T)
@@ -220,6 +222,7 @@ def test_bad_token_sets_flag():
     (G.FP32, 211, 64, 64, 4, 2, 3, 20),
     (G.BF16, 211, 512, 128, 2, 2, 4, 300),
     (G.BF16, 97, 64, 64, 1, 2, 2, 1),
+    (G.BF16, 301, 128, 512, 8, 2, 5, 40),
 ])
 def test_decode_matches_uncached(mode, V, n_ctx, d, h, L, B, T):
     """Forward over T-1 tokens into the cache, then one decode step of token T-1,

@@ -35,6 +35,11 @@
  *     embedding kernel zero-fills that row and raises a sticky device flag in
  *     the workspace that gpt2_read_device_flags reports and clears.
  *   - Concurrent calls must use distinct workspaces.
+ *   - Reproducibility (GPT2_BF16): with B*T > 64 rows a call is deterministic,
+ *     bit for bit.  With B*T <= 64 (the decode step, greedy generation) the
+ *     residual products split their K range over workgroups and add the parts
+ *     with fp32 atomics in no fixed order, so results may differ in the last
+ *     bits between runs.
  *   - Device pointers to weights, activations and the K/V cache must be
  *     16-byte aligned; token ids, targets, outputs of ids and fp32 logits /
  *     losses 4-byte aligned; the workspace 256-byte aligned (any hipMalloc or

@@ -46,7 +46,7 @@ struct EpiStoreF32 {
   }
 };
 
-// The head's fp32 logits through the 128x192 MFMA kernel, written in whole
+// The head's fp32 logits through the DMA-ring MFMA kernel, written in whole
 // 128-byte lines.  Rows of [M, N] start at arbitrary 4-byte phases (N is odd),
 // so plain column tiles share a partial line with their neighbours in every
 // row, and partial-line writes run at well under half the write bandwidth.
@@ -538,8 +538,9 @@ GPT2_DEV void tile_epilogue(const f32x16_t (&acc)[FN][FM], const typename Epi::C
   }
 }
 
-// ---------------------------------------------------------------- v3 schedule
-// Same tiles, loads and fragments as above, with the barrier moved: a K step's
+// ---------------------------------------------------------------- the kernel
+// Tiles, loads and fragments as described for V2Cfg.  Schedule per K step: the
+// step's MFMAs with the next step's fragment reads between them; a K step's
 // last MFMAs are issued after the barrier that publishes the next stage, so
 // the first fragment reads of stage kt+1 (and the barrier's own skew) overlap
 // them instead of leaving the matrix cores idle at every stage boundary.  The

@@ -169,3 +169,10 @@ def test_generate_argument_errors():
     assert call(2, 10, 5, G.KV(FAKE + 4, 1024)) == 8
     need = G.load().gpt2_generate_workspace_size(ctypes.byref(hp), G.BF16, 2)
     assert need > G.workspace_size(hp, G.BF16, 2, 1)   # the step's regions plus logits and tokens
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """No fallback path: without the built library every call site gets an error."""
+    monkeypatch.setattr(G, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        G.load(str(tmp_path / "libgpt2mi.so"))

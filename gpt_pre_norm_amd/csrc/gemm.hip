@@ -114,6 +114,20 @@ struct EpiLoss {
   GPT2_DEV void operator()(int, int, f32x4_t) const {}
 };
 
+// The head for greedy generation without its logits: per row m and per
+// (column tile, wave column) the largest logit and its column go to
+// part[m][slot] (the lowest column among equal values; NaN is never chosen
+// over a number); argmax_parts_kernel picks the best of a row's partials.
+struct EpiArgmax {
+  static constexpr bool kRowArgmax = true;
+  float2* part;  // [M][nparts]: value, column (as bits)
+  int N, nparts;
+  struct Ctx {};
+  GPT2_DEV Ctx load(int, int) const { return {}; }
+  GPT2_DEV void store(int, int, f32x4_t, Ctx) const {}
+  GPT2_DEV void operator()(int, int, f32x4_t) const {}
+};
+
 template <typename Tact>
 struct EpiBiasGelu {
   const Tact* bias;
@@ -424,6 +438,52 @@ GPT2_DEV void lse_epilogue(const f32x16_t (&acc)[FN][FM], const EpiLoss& epi, in
 }
 
 template <class Epi>
+constexpr bool row_argmax() {
+  if constexpr (requires { Epi::kRowArgmax; }) return Epi::kRowArgmax;
+  else return false;
+}
+
+// Epilogues that reduce rows straight from the accumulators (no stores of
+// the product, no epilogue reads).
+template <class Epi>
+constexpr bool row_reduce() {
+  return row_lse<Epi>() || row_argmax<Epi>();
+}
+
+// EpiArgmax at the end of a tile, from the MFMA layout described for
+// lse_epilogue.  A lane scans its columns in increasing order, so a strict
+// "greater" keeps the lowest column among equal values; the two lanes of a
+// token then combine with the same tie rule.
+template <int FM, int FN>
+GPT2_DEV void argmax_epilogue(const f32x16_t (&acc)[FN][FM], const EpiArgmax& epi, int M, int mw0, int nw0,
+                              int slot, int lane) {
+  const int r32 = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < FM; ++b) {
+    const int m = mw0 + b * 32 + r32;
+    float best = -INFINITY;
+    int bi = 0x7fffffff;  // no column yet: loses every tie
+#pragma unroll
+    for (int a = 0; a < FN; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = nw0 + a * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+        const float v = acc[a][b][r];
+        if (n < epi.N && (v > best || (v == best && n < bi))) {
+          best = v;
+          bi = n;
+        }
+      }
+    float v0, v1, i0, i1;
+    row_pair<32>(best, v0, v1);
+    row_pair<32>(__int_as_float(bi), i0, i1);
+    const int j0 = __float_as_int(i0), j1 = __float_as_int(i1);
+    const bool take1 = v1 > v0 || (v1 == v0 && j1 < j0);
+    if (kh == 0 && m < M) epi.part[(long long)m * epi.nparts + slot] = make_float2(take1 ? v1 : v0, take1 ? i1 : i0);
+  }
+}
+
+template <class Epi>
 constexpr bool row_store() {
   if constexpr (requires { Epi::kRowStore; }) return Epi::kRowStore;
   else return false;
@@ -663,7 +723,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_v3_kernel(const bf16
   }
   // the last K stage: no main-loop loads are waited for from here on
   typename Epi::Ctx cx[FN][FM][4];
-  if constexpr (!row_lse<Epi>() && hoist_ctx<Epi>())
+  if constexpr (!row_reduce<Epi>() && hoist_ctx<Epi>())
     tile_epilogue_loads<FM, FN>(cx, epi, M, N, m0 + wm * WM, n0 + wn * WN, lane);
   if (nk > 0) {
     const int kt = nk - 1;
@@ -675,11 +735,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_v3_kernel(const bf16
     // bounds, never consumed)
     step(1, lds + ((kt + 1) % STAGES) * C::STAGE_U4, 0);
   }
-  if constexpr (!row_lse<Epi>() && !hoist_ctx<Epi>())
+  if constexpr (!row_reduce<Epi>() && !hoist_ctx<Epi>())
     tile_epilogue_loads<FM, FN>(cx, epi, M, N, m0 + wm * WM, n0 + wn * WN, lane);
 
   if constexpr (row_lse<Epi>()) {
     lse_epilogue<FM, FN, WN>(acc, epi, M, m0 + wm * WM, n0 + wn * WN, tn_idx * WGN + wn, lane);
+  } else if constexpr (row_argmax<Epi>()) {
+    argmax_epilogue<FM, FN>(acc, epi, M, m0 + wm * WM, n0 + wn * WN, tn_idx * WGN + wn, lane);
   } else {
     __syncthreads();  // all waves are done reading the K stages
     tile_epilogue<FM, FN>(acc, cx, lds, epi, M, N, m0 + wm * WM, n0 + wn * WN, wave, lane);
@@ -888,9 +950,11 @@ template <class Epi>
 static void dispatch_bf16(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
                           hipStream_t s) {
   if (M <= 64) {
-    // wide outputs (the head): enough 64x128 tiles to stream W over every CU,
-    // X read once per tile instead of once per 32 columns
-    if (N >= 8192 && K % 64 == 0) {
+    // the head (fp32 logits) and other wide outputs: enough 64x128 tiles to
+    // stream W over every CU, X read once per tile instead of once per 32
+    // columns.  The head always takes this kernel, the one that the fused
+    // greedy choice (EpiArgmax) runs, so both see the same logits.
+    if ((N >= 8192 || std::is_same_v<Epi, EpiStoreF32>) && K % 64 == 0) {
       run_bf16_v3<64, 128, 64, 2, Epi, 2, 4>(X, W, M, N, K, epi, s);
       return;
     }
@@ -1016,6 +1080,15 @@ void launch_head_lse(const void* X, const void* W, int M, int N, int K, const in
                      float* tgt, hipStream_t s) {
   const EpiLoss epi{targets, (float2*)part, tgt, N, head_lse_parts(N)};
   run_bf16_v3<256, 256, 64, 2, EpiLoss, 4, 2>((const bf16_t*)X, (const bf16_t*)W, M, N, K, epi, s);
+}
+
+bool head_argmax_fused(bool bf16, int M, int K) { return bf16 && M <= 64 && K % 64 == 0; }
+
+int head_argmax_parts(int N) { return 4 * ((N + 127) / 128); }
+
+void launch_head_argmax(const void* X, const void* W, int M, int N, int K, void* part, hipStream_t s) {
+  const EpiArgmax epi{(float2*)part, N, head_argmax_parts(N)};
+  run_bf16_v3<64, 128, 64, 2, EpiArgmax, 2, 4>((const bf16_t*)X, (const bf16_t*)W, M, N, K, epi, s);
 }
 
 void launch_gemm(bool bf16, const void* X, const void* W, int M, int N, int K, const Epilogue& e,

@@ -65,14 +65,17 @@ Layout layout(const gpt2_hparams& hp, gpt2_mode mode, int B, int T) {
 // and the next tokens [B] int32.
 struct GenLayout {
   Layout step;
+  bool fused;  // the head reduces to (value, column) partials; no logits
   size_t logits, ids, total;
 };
 
 GenLayout gen_layout(const gpt2_hparams& hp, gpt2_mode mode, int B) {
   GenLayout G;
   G.step = layout(hp, mode, B, 1);
+  G.fused = head_argmax_fused(mode == GPT2_BF16, B, hp.n_embd);
   size_t off = G.step.total;
-  G.logits = off;  off += up((size_t)B * hp.n_vocab * 4);
+  G.logits = off;  // full logits rows, or the head's partials
+  off += up(G.fused ? (size_t)B * head_argmax_parts(hp.n_vocab) * 8 : (size_t)B * hp.n_vocab * 4);
   G.ids = off;     off += up((size_t)B * 4);
   G.total = off;
   return G;
@@ -447,8 +450,15 @@ gpt2_status gpt2_generate_greedy(const gpt2_hparams* hp, gpt2_mode mode, const g
   for (int i = 0; i < n_new; ++i) {
     // token i sits at position l_past + i; its logits choose token i + 1
     Run r{*hp, mode, B, 1, l_past + i, true, w, G.step, (hipStream_t)stream};
-    r.model(*W, i == 0 ? ids : next, logits, cache);
-    timed(K_ARGMAX, r.s, [&] { launch_argmax_rows(logits, B, hp->n_vocab, next, out, n_new, i, r.s); });
+    if (G.fused) {
+      const int parts = head_argmax_parts(hp->n_vocab);
+      r.trunk(*W, i == 0 ? ids : next, cache);
+      timed(K_GEMM_HEAD, r.s, [&] { launch_head_argmax(r.at(r.L.a), W->wte, B, hp->n_vocab, hp->n_embd, logits, r.s); });
+      timed(K_ARGMAX, r.s, [&] { launch_argmax_parts(logits, parts, B, hp->n_vocab, next, out, n_new, i, r.s); });
+    } else {
+      r.model(*W, i == 0 ? ids : next, logits, cache);
+      timed(K_ARGMAX, r.s, [&] { launch_argmax_rows(logits, B, hp->n_vocab, next, out, n_new, i, r.s); });
+    }
   }
   return hip_status();
 }

@@ -89,5 +89,14 @@ void launch_attn_decode_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H
 // index among equal maxima), for b < B.
 void launch_argmax_rows(const float* logits, int B, int V, int32_t* next_ids, int32_t* out, int out_stride,
                         int step, hipStream_t s);
+// The same choice without the logits (bf16, M <= 64, K % 64 == 0): the head
+// product X [M, K] against W [N, K] reduces each tile to per-row (value,
+// column) partials part [M][head_argmax_parts(N)] (float2, column as bits),
+// then launch_argmax_parts picks each row's best.
+bool head_argmax_fused(bool bf16, int M, int K);
+int head_argmax_parts(int N);
+void launch_head_argmax(const void* X, const void* W, int M, int N, int K, void* part, hipStream_t s);
+void launch_argmax_parts(const void* part, int nparts, int B, int V, int32_t* next_ids, int32_t* out,
+                         int out_stride, int step, hipStream_t s);
 
 }  // namespace gpt2

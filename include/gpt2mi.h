@@ -165,7 +165,8 @@ size_t gpt2_generate_workspace_size(const gpt2_hparams *hp, gpt2_mode mode, int3
  * (appending its K, V at that slot) and picks token i + 1 as the argmax of its
  * logits (lowest index among equal maxima), written to out[b * n_new + i]
  * (out: [B, n_new] int32, device).  Nothing is synchronised and no logits are
- * returned.  Requires n_new >= 1 and l_past + n_new <= min(n_ctx,
+ * returned; in GPT2_BF16 with B <= 64 none are written either (the head's
+ * tiles reduce to per-row maxima in the product itself).  Requires n_new >= 1 and l_past + n_new <= min(n_ctx,
  * cache->capacity), else GPT2_E_POSITION; ws_bytes >=
  * gpt2_generate_workspace_size(hp, mode, B). */
 gpt2_status gpt2_generate_greedy(const gpt2_hparams *hp, gpt2_mode mode, const gpt2_weights *W,

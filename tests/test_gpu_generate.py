@@ -91,6 +91,47 @@ def test_generate_matches_decode_steps():
     assert torch.equal(caches[0], caches[1])
 
 
+@pytest.mark.parametrize("case", ["all_zero", "two_rows"])
+def test_generate_ties_lowest_index(case):
+    """Tied logits: the device choice is the lowest column among equal maxima,
+    across tiles of the head product.  all_zero: wte = 0, so every logit is
+    exactly 0 and every chosen token is 0.  two_rows: wte = 0 except rows
+    300 and 9000 equal to v and rows 200 and 8000 equal to -v, so whatever the
+    sign of a position's logit for v, the maximum is a tie between two columns
+    in different tiles (300 or 200 must win); the loop must also match
+    host-driven steps with torch's argmax."""
+    mode, V, n_ctx, d, h, L, B, T0, n_new = G.BF16, 10007, 64, 128, 2, 1, 3, 5, 6
+    W = synth.model_weights(V, n_ctx, d, L, 1300, affine="random", bf16=True)
+    W["wte"][:] = 0.0
+    if case == "two_rows":
+        v = synth.normal((d,), 0.5, 1301, 0, bf16=True)
+        W["wte"][300] = v
+        W["wte"][9000] = v
+        W["wte"][200] = -v
+        W["wte"][8000] = -v
+    Wd, hp = G.upload_model(W, mode), hp_of(V, n_ctx, d, h, L)
+    prompt = synth.ids_input((B, T0), V, 1302)
+    cap = T0 + n_new
+    caches = [new_cache(mode, B, L, h, cap, d // h) for _ in range(2)]
+    for c in caches:
+        _, st = run_prefill(mode, hp, Wd, prompt[:, :T0 - 1], 0, c, cap)
+        assert st == 0
+    gen = _generate(mode, hp, Wd, prompt[:, T0 - 1], T0 - 1, n_new, caches[0], cap)
+    if case == "all_zero":
+        assert (gen == 0).all(), gen
+        return
+    tok = prompt[:, T0 - 1]
+    ref = []
+    for i in range(n_new):
+        logits = run_decode(mode, hp, Wd, tok, T0 - 1 + i, caches[1], cap)
+        tok = logits[:, 0].argmax(-1).int().cpu().numpy()
+        ref.append(tok)
+    ref = np.stack(ref, 1)
+    log(f"  two tied pairs: chosen {np.unique(gen)}")
+    assert np.isin(gen, (200, 300)).all(), gen
+    assert np.array_equal(gen, ref), (gen, ref)
+
+
 def test_generate_gpt2s_full():
     """GPT-2 small, 64 sequences with a random past of 1000 positions, 16
     greedy tokens; sequences 0 and 37 replayed by the oracle's cached decode."""

@@ -108,10 +108,17 @@ def hparams(n_vocab=50257, n_ctx=1024, n_embd=768, n_head=12, n_layer=12, eps=1e
 
 
 def _ptr(t) -> int | None:
+    """Device address of a tensor (None and raw integer addresses pass through).
+    The C ABI takes dense row-major device buffers: a host tensor or a strided
+    view is refused here rather than read as if it were dense."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
     return t.data_ptr()
 
 

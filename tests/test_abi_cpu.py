@@ -176,3 +176,10 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(G, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         G.load(str(tmp_path / "libgpt2mi.so"))
+
+
+def test_binding_refuses_host_and_strided_tensors():
+    import torch
+    with pytest.raises(ValueError, match="device tensor"):
+        G._ptr(torch.zeros(4))
+    assert G._ptr(None) is None and G._ptr(FAKE) == FAKE

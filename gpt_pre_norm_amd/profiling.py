@@ -17,6 +17,14 @@ Commands (run from the repository root):
       (FETCH_SIZE, WRITE_SIZE), each scaled by what the same counter reads for
       the calibration copy.  The record carries a hash of the kernel sources,
       so bench.py ignores it once the kernels change.
+
+  python -m gpt_pre_norm_amd.profiling core --pmc CSV --trace CSV --out TXT
+         --command "..."
+      Per kernel kind, from one --pmc run with --kernel-trace: matrix-core
+      busy cycles against the launch's duration (at the nominal 2.4 GHz, so a
+      lower bound on the busy fraction), the bf16 MFMA work the counters saw
+      against the algorithmic flops, and LDS bank-conflict cycles against LDS
+      active cycles.
 """
 from __future__ import annotations
 
@@ -169,6 +177,53 @@ def cmd_traffic(args):
                   f"write {v['write_bytes'] / 1e6:10.2f} MB")
 
 
+CORE_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_LDS_BANK_CONFLICT",
+                 "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS")
+N_SIMD = 1024      # 256 CUs x 4 SIMDs
+CLOCK_HZ = 2.4e9   # nominal peak engine clock
+
+
+def cmd_core(args):
+    from gpt_pre_norm_amd import roofline as R
+    from gpt_pre_norm_amd.workloads import WORKLOADS
+    dur = {}
+    for r in csv.DictReader(open(args.trace)):
+        dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    vals = {c: {did: v for did, _, _, v in read_pmc(args.pmc, c)} for c in CORE_COUNTERS}
+    base = read_pmc(args.pmc, CORE_COUNTERS[0])
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for did, phase, k, grid, _ in classify(base):
+        if did not in dur or not k.startswith(("gemm", "attn", "layernorm", "embed")):
+            continue
+        d = per[(phase, k)]
+        d["n"] += 1
+        d["sec"] += dur[did]
+        for c in CORE_COUNTERS:
+            d[c] += vals[c].get(did, 0.0)
+    fw, dw = WORKLOADS["gpt2s_fwd_b8_t1024"], WORKLOADS["gpt2s_decode_b64_p1023"]
+    lines = ["# matrix-core and LDS counters per kernel kind (rocprofv3 --pmc with --kernel-trace)",
+             f"# command: {args.command}",
+             "# mfma_busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x duration x 2.4 GHz), a lower bound",
+             "# mops_vs_alg: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / algorithmic flops of the launch",
+             "# lds_conflict: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE",
+             "#",
+             f"{'phase':8s} {'kernel':18s} {'launches':>8s} {'avg_us':>9s} {'mfma_busy':>10s} {'mops_vs_alg':>12s} "
+             f"{'lds_conflict':>13s} {'lds_insts/launch':>17s}"]
+    for (phase, k), d in sorted(per.items()):
+        n = int(d["n"])
+        avg = d["sec"] / n
+        busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * d["sec"] * CLOCK_HZ)
+        wl = fw if phase == "forward" else dw
+        B, T = (wl.B, wl.T) if phase == "forward" else (wl.B, 1)
+        f, _ = R.kernel_work(k, B=B, T=T, d=wl.d, h=wl.h, V=wl.n_vocab, l_past=getattr(wl, "l_past", 0))
+        mops = d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / (f * n) if f else float("nan")
+        conf = d["SQ_LDS_BANK_CONFLICT"] / d["SQ_LDS_IDX_ACTIVE"] if d["SQ_LDS_IDX_ACTIVE"] else 0.0
+        lines.append(f"{phase:8s} {k:18s} {n:8d} {avg * 1e6:9.2f} {busy:10.3f} {mops:12.3f} {conf:13.4f} "
+                     f"{d['SQ_INSTS_LDS'] / n:17.4g}")
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -182,8 +237,11 @@ def main(argv=None):
     for a in ("--fetch", "--write", "--cal-fetch", "--cal-write", "--out", "--command"):
         t.add_argument(a, required=True)
     t.add_argument("--cal-mib", type=int, default=1024)
+    c2 = sub.add_parser("core")
+    for a in ("--pmc", "--trace", "--out", "--command"):
+        c2.add_argument(a, required=True)
     args = ap.parse_args(argv)
-    {"calibrate": cmd_calibrate, "stats": cmd_stats, "traffic": cmd_traffic}[args.cmd](args)
+    {"calibrate": cmd_calibrate, "stats": cmd_stats, "traffic": cmd_traffic, "core": cmd_core}[args.cmd](args)
 
 
 if __name__ == "__main__":

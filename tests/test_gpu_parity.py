@@ -41,7 +41,9 @@ def test_block_d64_fp32(affine):
     check("present", pres, opres, G.FP32)
 
 
-@pytest.mark.parametrize("B,T,d,h", [(3, 77, 96, 3), (1, 130, 128, 2), (2, 1, 32, 8)])
+@pytest.mark.parametrize("B,T,d,h", [(3, 77, 96, 3), (1, 130, 128, 2), (2, 1, 32, 8),
+                                     # widest head (d_h 128) and widest rows (n_embd 2048)
+                                     (1, 40, 256, 2), (1, 12, 2048, 16)])
 def test_block_fp32_ragged(B, T, d, h):
     x = synth.hidden_input((B, T, d), 100 + T)
     w = synth.block_weights(d, 100 + T, affine="random")
@@ -108,8 +110,11 @@ def _small_model(mode, V, n_ctx, d, h, L, seed):
     # wider rows through the line-aligned head: d = 256 and 768, one partial row tile
     (G.BF16, 2001, 128, 256, 4, 1, 2, 100),
     (G.BF16, 777, 128, 768, 12, 1, 1, 100),
-    # 60 rows: the skinny products with the LayerNorm in their prologue
+    # 60 rows: the decode-sized (skinny) products and the 64x128 head
     (G.BF16, 2001, 128, 256, 4, 1, 2, 30),
+    # the widest supported rows (n_embd 2048, 32 heads): LayerNorm at 8 groups
+    # per lane, the register-staged product where the skinny one cannot take K
+    (G.BF16, 301, 64, 2048, 32, 1, 1, 20),
 ])
 def test_forward_small(mode, V, n_ctx, d, h, L, B, T):
     W, Wd, hp = _small_model(mode, V, n_ctx, d, h, L, 400 + T)

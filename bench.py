@@ -70,8 +70,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(batch sharding is described in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(it would shard the batch, one replica per GPU); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -24,7 +24,7 @@ Sources (web pages, cited by title and section):
   embedding sum with positions offset by the cache length, the stacked
   ``present`` of shape [B, L, 2, h, T, d_h], ln_f and the tied projection.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 * GELU is the tanh approximation (the pages only name ``gelu``).
 * Key m is visible to query i iff m <= l_past + i (absolute positions).
 * Weights of every linear layer are stored [out, in]; y = x W^T + b.

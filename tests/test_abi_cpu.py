@@ -183,3 +183,13 @@ def test_binding_refuses_host_and_strided_tensors():
     with pytest.raises(ValueError, match="device tensor"):
         G._ptr(torch.zeros(4))
     assert G._ptr(None) is None and G._ptr(FAKE) == FAKE
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """One GPU only: --gpus N > 1 exits with a message before touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU only" in r.stderr

@@ -48,14 +48,17 @@ def _assert_greedy(tokens, logits, mode, what):
 @pytest.mark.parametrize("mode,V,n_ctx,d,h,L,B,T0,n_new", [
     (G.FP32, 301, 128, 64, 4, 2, 2, 9, 12),
     (G.BF16, 1001, 256, 128, 2, 2, 3, 40, 24),
+    # from an empty cache (the first token at position 0) to the last position
+    (G.BF16, 501, 16, 128, 2, 2, 2, 1, 16),
 ])
 def test_generate_greedy_valid(mode, V, n_ctx, d, h, L, B, T0, n_new):
     W, Wd, hp = _small_model(mode, V, n_ctx, d, h, L, 1100 + T0)
     prompt = synth.ids_input((B, T0), V, 1101 + T0)
-    cap = T0 + n_new + 3
+    cap = min(T0 + n_new + 3, n_ctx)
     cache = new_cache(mode, B, L, h, cap, d // h)
-    _, st = run_prefill(mode, hp, Wd, prompt[:, :T0 - 1], 0, cache, cap)
-    assert st == 0
+    if T0 > 1:
+        _, st = run_prefill(mode, hp, Wd, prompt[:, :T0 - 1], 0, cache, cap)
+        assert st == 0
     log(f"generate mode={mode} d={d} L={L} B={B} from position {T0 - 1}, {n_new} tokens")
     gen = _generate(mode, hp, Wd, prompt[:, T0 - 1], T0 - 1, n_new, cache, cap)
     assert ((gen >= 0) & (gen < V)).all()

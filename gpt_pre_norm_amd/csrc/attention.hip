@@ -106,23 +106,33 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
           bf16x8_t, *reinterpret_cast<const uint4*>(qbase + (long long)t * D + 16 * ds + 8 * kh));
   }
 
-  // loads: this wave fills K and V rows 8*wave.. and 8*(wave+4)..
+  // loads: this wave fills K and V rows 8*wave.. and 8*(wave+4).. of each
+  // tile through buffer loads into LDS: the lane's byte offset within a tile
+  // is fixed, the tile's offset is a scalar, and rows at or past kend read as
+  // zeros (the resource ends there), which the mask then drops.
   const int lrow = lane >> 3, lpc = lane & 7;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const __amdgpu_buffer_rsrc_t krsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, kend * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, kend * D * 2, 0x00020000);
+  int koff[2], voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 8 * (wave + 4 * i) + lrow;
+    koff[i] = (row * D + (lpc ^ ((row >> 1) & 7)) * 8) * 2;
+    voff[i] = (row * D + (lpc ^ v_swz(row)) * 8) * 2;
+  }
   auto issue = [&](int kb, int st) {
-    const int key0 = kb * 64;
+    const int tile = kb * 64 * D * 2;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int g = wave + 4 * i;
-      const int row = 8 * g + lrow;
-      const int key = min(key0 + row, kend - 1);
-      const int ck = lpc ^ ((row >> 1) & 7);
-      const int cv = lpc ^ v_swz(row);
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + (long long)key * D + ck * 8),
-                                       (__attribute__((address_space(3))) void*)(lds + st * kAttnStageU4 + g * 64),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + (long long)key * D + cv * 8),
-                                       (__attribute__((address_space(3))) void*)(lds + st * kAttnStageU4 + 512 + g * 64),
-                                       16, 0, 0);
+      const int g = wave_s + 4 * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          krsrc, (__attribute__((address_space(3))) void*)(lds + st * kAttnStageU4 + g * 64), 16, koff[i], tile, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vrsrc, (__attribute__((address_space(3))) void*)(lds + st * kAttnStageU4 + 512 + g * 64), 16, voff[i], tile,
+          0, 0);
     }
   };
   // transposing-read addresses (bytes within a V tile): lane group G = lane/16
@@ -187,11 +197,12 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
       // and the O / sum rescale is skipped for most tiles.  Both use the same
       // mref, so the final O / sum is the softmax.
       if (key0 + 63 > l_past + qw0) {
+        const int lim = qpos - key0 - 8 * kh;  // key offsets above lim are masked
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (key0 + 32 * kk + 16 * (r >> 3) + 8 * kh + (r & 7) > qpos) s[kk][r] = -INFINITY;
+            if (32 * kk + 16 * (r >> 3) + (r & 7) > lim) s[kk][r] = -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll

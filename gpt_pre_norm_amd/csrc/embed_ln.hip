@@ -6,8 +6,9 @@
 // then gain and bias (Open Model Atlas, norm() excerpt; "Decoder Block", How it works).
 //
 // Both are HBM-bound streaming kernels: 4 elements per lane per access
-// (16 B fp32 / 8 B bf16), rows held in registers, no LDS.  The other
-// LayerNorms of the forward run inside the residual products (gemm.hip).
+// (16 B fp32 / 8 B bf16), rows held in registers, no LDS.  The first block's
+// LN1 runs inside the embedding kernel; every other LayerNorm (LN2, the
+// later LN1s, ln_f) is a launch of the row kernel.
 #include "kernels.h"
 
 namespace gpt2 {

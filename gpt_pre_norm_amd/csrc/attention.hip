@@ -363,10 +363,11 @@ void launch_attn_rows_f32(const float* q, KvView kv, float* o, int B, int H, int
 // One workgroup of NW waves per (sequence, head) streams the whole cache row
 // range 0 .. l_past: wave w takes keys [8 RP (w + NW j), +8 RP).  Inside a
 // wave, 8 lanes share a key row (8 dims each); a lane issues its RP K and RP V
-// row loads together (RP = 16: 32 KB in flight per wave).
+// row loads together (RP = 8: 16 KB in flight per wave, 100 VGPRs, so four
+// waves per SIMD and every workgroup of a 768-workgroup launch resident).
 // Each wave keeps an online softmax (running max, partial sums per lane);
 // the waves then merge through LDS, so no second kernel is needed.
-constexpr int kDecWaves = 4, kDecRows = 16;  // measured best at 1024 keys, d_h 64
+constexpr int kDecWaves = 8, kDecRows = 8;  // measured best at 1024 keys, d_h 64
 
 // NW waves; RP key rows per lane per pass (RP/8 passes of 8 rows); PF: the
 // next pass's rows are loaded before the current pass is reduced.

@@ -752,12 +752,14 @@ template <int BM, int BN, int BK, int STAGES, class Epi, int WGM, int WGN>
 static void run_bf16_v3(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
                         hipStream_t s) {
   using C = V2Cfg<BM, BN, BK, STAGES, WGM * WGN>;
-  static bool attr_set = false;  // one-time, per template instance
-  if (!attr_set) {
+  // once per template instance; a function-local static is initialised once
+  // even when several host threads launch concurrently
+  static const bool attr_set = [] {
     (void)hipFuncSetAttribute((const void*)gemm_bf16_v3_kernel<BM, BN, BK, STAGES, WGM, WGN, Epi>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-    attr_set = true;
-  }
+    return true;
+  }();
+  (void)attr_set;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN + (line_aligned<Epi>() ? 1 : 0);
   gemm_bf16_v3_kernel<BM, BN, BK, STAGES, WGM, WGN, Epi>
       <<<tiles_m * tiles_n, 64 * WGM * WGN, C::LDS_BYTES, s>>>(X, W, M, N, K, epi, tiles_m, tiles_n);
@@ -890,12 +892,12 @@ template <int NT, class Epi>
 static void run_skinny(const bf16_t* X, const bf16_t* W, int M, int N, int K, int S, const Epi& epi,
                        hipStream_t s) {
   const size_t lds = (size_t)(64 + NT) * (K / S) * 2;
-  static bool attr_set = false;  // one-time, per template instance
-  if (!attr_set) {
+  static const bool attr_set = [] {  // once per template instance, thread-safe
     (void)hipFuncSetAttribute((const void*)gemm_skinny_kernel<NT, Epi>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_set = true;
-  }
+    return true;
+  }();
+  (void)attr_set;
   const int nslices = (N + NT - 1) / NT;
   gemm_skinny_kernel<NT, Epi><<<nslices * S, 256, lds, s>>>(X, W, M, N, K, S, epi,
                                                              FastDiv::make((uint32_t)(K / S / 8)));

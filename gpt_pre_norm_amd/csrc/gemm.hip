@@ -891,7 +891,9 @@ static int skinny_splits(int K, int nslices = 0, int min_wg = 0) {
 template <int NT, class Epi>
 static void run_skinny(const bf16_t* X, const bf16_t* W, int M, int N, int K, int S, const Epi& epi,
                        hipStream_t s) {
-  const size_t lds = (size_t)(64 + NT) * (K / S) * 2;
+  // the tile, and after the MFMAs the four waves' partial sums
+  // (4 waves x NT/16 x 4 fragments x 64 lanes x 16 B = NT KB) in the same space
+  const size_t lds = std::max((size_t)(64 + NT) * (K / S) * 2, (size_t)NT * 1024);
   static const bool attr_set = [] {  // once per template instance, thread-safe
     (void)hipFuncSetAttribute((const void*)gemm_skinny_kernel<NT, Epi>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);

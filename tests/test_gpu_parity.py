@@ -228,6 +228,11 @@ def test_bad_token_sets_flag():
     (G.BF16, 211, 512, 128, 2, 2, 4, 300),
     (G.BF16, 97, 64, 64, 1, 2, 2, 1),
     (G.BF16, 301, 128, 512, 8, 2, 5, 40),
+    # 777 keys: a ragged second pass of the decode attention (512 keys per
+    # workgroup pass), some waves with no keys in it
+    (G.BF16, 211, 1024, 128, 2, 2, 3, 777),
+    # B = 70 > 64: the decode step's products take the block kernels
+    (G.BF16, 211, 128, 128, 2, 2, 70, 50),
 ])
 def test_decode_matches_uncached(mode, V, n_ctx, d, h, L, B, T):
     """Forward over T-1 tokens into the cache, then one decode step of token T-1,

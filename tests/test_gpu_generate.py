@@ -50,6 +50,8 @@ def _assert_greedy(tokens, logits, mode, what):
     (G.BF16, 1001, 256, 128, 2, 2, 3, 40, 24),
     # from an empty cache (the first token at position 0) to the last position
     (G.BF16, 501, 16, 128, 2, 2, 2, 1, 16),
+    # B = 66 > 64: full bf16 logits, then the row argmax kernel
+    (G.BF16, 211, 128, 128, 2, 2, 66, 20, 6),
 ])
 def test_generate_greedy_valid(mode, V, n_ctx, d, h, L, B, T0, n_new):
     W, Wd, hp = _small_model(mode, V, n_ctx, d, h, L, 1100 + T0)

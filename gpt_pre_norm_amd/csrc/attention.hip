@@ -14,7 +14,7 @@
 //  * attn_rows_f32: one wave per query row with a full (max-subtracted)
 //    softmax, for the fp32 mode.
 //  * attn_decode_bf16: one new query per (sequence, head) streaming the cache
-//    with one 4-wave workgroup per (sequence, head); the waves' online
+//    with one 8-wave workgroup per (sequence, head); the waves' online
 //    softmax states merge in LDS.
 #include "kernels.h"
 
@@ -355,6 +355,14 @@ void launch_attn_rows_f32(const float* q, KvView kv, float* o, int B, int H, int
   const long long rows = (long long)B * H * T;
   const int maxk = l_past + T;
   const int blocks = (int)((rows + 3) / 4);
+  // a row of scores per wave: 4 waves x maxk x 4 B, up to 128 KB at the
+  // 8192-key limit the entry points enforce, beyond the 64 KB default
+  static const bool attr_set = [] {  // once, thread-safe
+    (void)hipFuncSetAttribute((const void*)attn_rows_f32_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              4 * 8192 * (int)sizeof(float));
+    return true;
+  }();
+  (void)attr_set;
   attn_rows_f32_kernel<<<blocks, 256, 4 * maxk * sizeof(float), s>>>(q, kv, o, B, H, T, d_head,
                                                                      l_past, maxk);
 }

@@ -6,7 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "common.cuh"
+#include "common.h"
 
 namespace gpt2 {
 

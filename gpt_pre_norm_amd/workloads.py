@@ -59,6 +59,18 @@ WORKLOADS = {
         "gpt2s_decode_b64_p1023", "decode", BF16, 50257, 1024, 768, 12, 12, 64, 1, l_past=1023, seed=3,
         resid_scale=1 / math.sqrt(24),
         note="GPT-2 small cached decode, bf16, 64 sequences at position 1023, past ~ N(0,1)"),
+    # The other depths of the published table, L = 24 and 36; the pages print
+    # no widths for them: d = 1024 (16 heads) and d = 1280 (20 heads), head
+    # width 64 and a 4d MLP as at every depth, residual projections scaled by
+    # 1/sqrt(2L), B = 4 like the 48-layer workload.
+    "gpt2_l24_d1024_fwd_b4_t1024": Workload(
+        "gpt2_l24_d1024_fwd_b4_t1024", "forward", BF16, 50257, 1024, 1024, 16, 24, 4, 1024, seed=5,
+        resid_scale=1 / math.sqrt(48),
+        note="24 layers, d=1024, 16 heads, bf16, ids [4, 1024], logits fp32 [4, 1024, 50257]"),
+    "gpt2_l36_d1280_fwd_b4_t1024": Workload(
+        "gpt2_l36_d1280_fwd_b4_t1024", "forward", BF16, 50257, 1024, 1280, 20, 36, 4, 1024, seed=6,
+        resid_scale=1 / math.sqrt(72),
+        note="36 layers, d=1280, 20 heads, bf16, ids [4, 1024], logits fp32 [4, 1024, 50257]"),
     "gpt2_l48_d1600_fwd_b4_t1024": Workload(
         "gpt2_l48_d1600_fwd_b4_t1024", "forward", BF16, 50257, 1024, 1600, 25, 48, 4, 1024, seed=4,
         resid_scale=1 / math.sqrt(96),

@@ -36,12 +36,45 @@ def argmax_agreement(g_logits, o_logits, tol=TOL_BF16_ABS):
     """(tolerant, raw): a row agrees tolerantly when the oracle's logit at the
     GPU's argmax is within tol of the oracle's maximum (several tokens are
     correct within the stated logit tolerance); raw is plain argmax equality."""
+    s = argmax_stats(g_logits, o_logits, tol)
+    return s["tolerant"], s["raw"]
+
+
+def argmax_stats(g_logits, o_logits, tol=TOL_BF16_ABS):
+    """Argmax agreement of GPU logits with the oracle's, row by row:
+    tolerant (the oracle's logit at the GPU's choice within tol of its max),
+    raw (equal argmax), and gap-conditioned (raw agreement over the rows whose
+    oracle top-1 / top-2 gap exceeds 2 tol: there no error within the logit
+    tolerance can change the choice, so every such row must agree)."""
     g = np.asarray(g_logits).reshape(-1, g_logits.shape[-1])
     o = np.asarray(o_logits, np.float64).reshape(-1, o_logits.shape[-1])
-    ga = g.argmax(-1)
-    tolerant = (o[np.arange(len(ga)), ga] >= o.max(-1) - tol).mean()
-    raw = (ga == o.argmax(-1)).mean()
-    return float(tolerant), float(raw)
+    rows = np.arange(len(g))
+    ga, oa = g.argmax(-1), o.argmax(-1)
+    top2 = np.partition(o, -2, axis=-1)[:, -2:]
+    gap = top2[:, 1] - top2[:, 0]
+    wide = gap > 2 * tol
+    return {"rows": int(len(g)),
+            "tolerant": float((o[rows, ga] >= o.max(-1) - tol).mean()),
+            "raw": float((ga == oa).mean()),
+            "wide_rows": int(wide.sum()),
+            "wide_agree": float((ga[wide] == oa[wide]).mean()) if wide.any() else 1.0}
+
+
+def check_argmax(g_logits, o_logits, mode, min_rows=0):
+    """The argmax-agreement gate: >= 99.9% of rows agree (tolerant reading in
+    bf16 mode, raw argmax in fp32 mode), and every row whose oracle top-1 /
+    top-2 gap exceeds twice the bf16 logit tolerance agrees exactly.
+    min_rows: the gate is only resolved with at least that many rows."""
+    s = argmax_stats(g_logits, o_logits)
+    log(f"  argmax over {s['rows']} rows: tolerant {s['tolerant']:.4f} raw {s['raw']:.4f}; "
+        f"gap > {2 * TOL_BF16_ABS:g}: {s['wide_rows']} rows, agreement {s['wide_agree']:.4f}")
+    assert s["rows"] >= min_rows, (s["rows"], min_rows)
+    assert s["wide_agree"] == 1.0, s
+    if mode == G.FP32:
+        assert s["raw"] >= 0.999, s
+    else:
+        assert s["tolerant"] >= 0.999, s
+    return s
 
 
 def check(name, g, o, mode):

@@ -3,8 +3,10 @@
 Small cases span several GEMM / attention tiles and a ragged tail; the
 full-size cases run the workloads bench.py times and compare the sequences the
 oracle recomputes (sampled rows for logits).  Gates: fp32 mode max relative
-error <= 1e-4; bf16 mode max absolute error <= 3e-2 and argmax agreement
-(tolerant reading) >= 99.9%.
+error <= 1e-4 and raw argmax agreement >= 99.9%; bf16 mode max absolute error
+<= 3e-2 and argmax agreement (tolerant reading) >= 99.9%; in both, every row
+whose oracle top-1 / top-2 logit gap exceeds 6e-2 picks the oracle's token.
+The full-size forward workloads are gated on at least 1000 oracle rows each.
 """
 import numpy as np
 import pytest
@@ -13,8 +15,8 @@ import torch
 from gpt_pre_norm_amd import gpt2mi as G
 from gpt_pre_norm_amd import synth
 from gpt_pre_norm_amd.workloads import WORKLOADS, block_inputs, model_inputs, past_for_sequence
-from gpu_helpers import (TOL_BF16_ABS, argmax_agreement, check, hp_of, log, new_cache, run_block,
-                         run_decode, run_forward, to_np)
+from gpu_helpers import (TOL_BF16_ABS, check, check_argmax, hp_of, log, new_cache, run_block, run_decode,
+                         run_forward, to_np)
 from oracle import gpt2_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -52,6 +54,41 @@ def test_block_fp32_ragged(B, T, d, h):
     oy, opres = O.block_forward(x, w, h)
     check("y", y, oy, G.FP32)
     check("present", pres, opres, G.FP32)
+
+
+def test_block_fp32_gelu_is_tanh_form():
+    """The GELU form: c_fc pre-activations are placed within 0.35 of +-2.7,
+    where the tanh approximation and the erf form differ by 4e-4 to 4.7e-4,
+    and one-hot mlp.c_proj rows copy single GELU outputs into y.  The kernel
+    must match the tanh-form oracle within 2e-5 at every such element, so an
+    erf-form kernel would miss by more than 3e-4 ("GPT-2 Block - TorchCode",
+    Requirements, names the erf GELU; the tanh form is the reading taken)."""
+    B, T, d, h = 2, 40, 64, 4
+    x = synth.hidden_input((B, T, d), 150)
+    w = synth.block_weights(d, 150, affine="default")
+    for k in ("attn_w", "attn_b", "proj_w", "proj_b", "fc2_b"):
+        w[k] = np.zeros_like(w[k])  # attention adds nothing: x1 = x
+    rng = np.random.default_rng(150)
+    w["fc_w"] = (rng.standard_normal(w["fc_w"].shape) * 0.005).astype(np.float32)
+    sign = np.where(np.arange(4 * d) % 2 == 0, 1.0, -1.0)
+    w["fc_b"] = (sign * (2.7 + rng.uniform(-0.15, 0.15, 4 * d))).astype(np.float32)
+    pick = 4 * np.arange(d) + np.arange(d) % 2  # output i copies hidden unit pick[i]
+    fc2 = np.zeros((d, 4 * d), np.float32)
+    fc2[np.arange(d), pick] = 1.0
+    w["fc2_w"] = fc2
+    y, _ = run_block(G.FP32, d, h, x, w)
+    oy, _ = O.block_forward(x, w, h)
+    u = O.linear(O.layer_norm(x, w["ln2_g"], w["ln2_b"]), w["fc_w"], w["fc_b"])[..., pick]
+    assert np.all((np.abs(u) > 2.35) & (np.abs(u) < 3.05)), (np.abs(u).min(), np.abs(u).max())
+    import scipy.special
+    erf_form = 0.5 * u * (1.0 + scipy.special.erf(u / np.sqrt(2.0)))
+    ey = x + erf_form
+    sep = np.abs(oy - ey)
+    err = np.abs(y.astype(np.float64) - oy)
+    log(f"  gelu tanh vs erf separation min {sep.min():.3e}; kernel error vs tanh form max {err.max():.3e}")
+    assert sep.min() > 3e-4
+    assert err.max() < 2e-5
+    check("y", y, oy, G.FP32)
 
 
 @pytest.mark.parametrize("B,T,d", [(2, 200, 768), (3, 129, 128), (1, 1, 64), (2, 64, 192)])
@@ -126,15 +163,29 @@ def test_forward_small(mode, V, n_ctx, d, h, L, B, T):
     ol, opres = O.model_forward(ids, W, h)
     check("logits", to_np(logits), ol, mode)
     check("present", to_np(cache)[..., :T, :], opres, mode)
-    if mode == G.BF16:
-        tol, raw = argmax_agreement(to_np(logits), ol)
-        log(f"  argmax agreement tolerant {tol:.4f} raw {raw:.4f}")
-        assert tol >= 0.999
+    check_argmax(to_np(logits), ol, mode)
+
+
+def test_forward_fp32_long():
+    """fp32 mode over 1100 positions: the row-wise attention at more than 1024
+    keys (its scores fill 17.6 KB of LDS per wave), and raw argmax agreement
+    resolved over at least 1000 rows."""
+    V, n_ctx, d, h, L, B, T = 2001, 1152, 128, 4, 2, 1, 1100
+    W, Wd, hp = _small_model(G.FP32, V, n_ctx, d, h, L, 450)
+    ids = synth.ids_input((B, T), V, 451)
+    cache = new_cache(G.FP32, B, L, h, n_ctx, d // h)
+    log(f"forward fp32 V={V} d={d} h={h} L={L} B={B} T={T}")
+    logits, st = run_forward(G.FP32, hp, Wd, ids, cache=cache, capacity=n_ctx)
+    assert st == 0
+    ol, opres = O.model_forward(ids, W, h)
+    check("logits", to_np(logits), ol, G.FP32)
+    check("present", to_np(cache)[..., :T, :], opres, G.FP32)
+    check_argmax(to_np(logits), ol, G.FP32, min_rows=1000)
 
 
 def test_forward_gpt2s_full():
     """GPT-2 small forward at full size (B=8, T=1024, V=50257); sequences 0 and 5
-    recomputed by the oracle, 96 sampled logit rows each."""
+    recomputed by the oracle, every logit row (2048 rows for the argmax gate)."""
     wl = WORKLOADS["gpt2s_fwd_b8_t1024"]
     ids, W = model_inputs(wl)
     Wd = G.upload_model(W, wl.mode)
@@ -143,49 +194,45 @@ def test_forward_gpt2s_full():
     log("forward gpt2-small full size")
     logits, st = run_forward(wl.mode, hp, Wd, ids, cache=cache, capacity=wl.n_ctx)
     assert st == 0
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 1, 511, 1022, 1023], rng.integers(0, 1024, 91)]))
-    g_all = []
-    o_all = []
+    g_all, o_all = [], []
     for b in (0, 5):
-        ol, opres = O.model_forward(ids[b:b + 1], W, wl.h, logit_rows=rows)
-        g = to_np(logits[b, torch.from_numpy(rows).cuda()])
-        check(f"logits[{b}] ({len(rows)} rows)", g, ol, wl.mode)
+        ol, opres = O.model_forward(ids[b:b + 1], W, wl.h)
+        g = to_np(logits[b:b + 1])
+        check(f"logits[{b}] (all {wl.T} rows)", g, ol, wl.mode)
         check(f"present[{b}]", to_np(cache[b:b + 1]), opres, wl.mode)
-        g_all.append(g)
-        o_all.append(ol)
-    tol, raw = argmax_agreement(np.concatenate(g_all), np.concatenate(o_all))
-    log(f"  argmax agreement tolerant {tol:.4f} raw {raw:.4f}")
-    assert tol >= 0.999
+        g_all.append(g[0])
+        o_all.append(ol[0])
+        del ol, opres
+    check_argmax(np.concatenate(g_all), np.concatenate(o_all), wl.mode, min_rows=1000)
 
 
-def test_forward_l48_d1600_full():
-    """The widest published depth at full size (L=48, d=1600, 25 heads, B=4,
-    T=1024): the oracle recomputes the first 192 positions of sequence 0 and
-    the first 96 of sequence 3 (logits on sampled rows, cache slots in full);
-    positions past them are checked through causality: a run on the first 192
-    tokens reproduces the full run's rows bit for bit."""
-    wl = WORKLOADS["gpt2_l48_d1600_fwd_b4_t1024"]
+@pytest.mark.parametrize("name", ["gpt2_l24_d1024_fwd_b4_t1024", "gpt2_l36_d1280_fwd_b4_t1024",
+                                  "gpt2_l48_d1600_fwd_b4_t1024"])
+def test_forward_deep_full(name):
+    """The other published depths at full size (L=24 d=1024, L=36 d=1280,
+    L=48 d=1600; B=4, T=1024): the oracle recomputes sequence 0 in full (all
+    1024 logit rows for the argmax gate, every cache slot) and the first 96
+    positions of sequence 3; the remaining positions of sequences 1-3 are
+    covered through causality: a run on the first 192 tokens reproduces the
+    full run's rows and cache slots bit for bit."""
+    wl = WORKLOADS[name]
     ids, W = model_inputs(wl)
     Wd = G.upload_model(W, wl.mode)
     hp = hp_of(wl.n_vocab, wl.n_ctx, wl.d, wl.h, wl.L)
     cache = new_cache(wl.mode, wl.B, wl.L, wl.h, wl.n_ctx, wl.dh)
-    log("forward L=48 d=1600 full size")
+    log(f"forward {name} full size")
     logits, st = run_forward(wl.mode, hp, Wd, ids, cache=cache, capacity=wl.n_ctx)
     assert st == 0
-    rng = np.random.default_rng(1)
     g_all, o_all = [], []
-    for b, P in ((0, 192), (3, 96)):
-        rows = np.unique(np.concatenate([[0, 1, P // 2, P - 1], rng.integers(0, P, 16)]))
-        ol, opres = O.model_forward(ids[b:b + 1, :P], W, wl.h, logit_rows=rows)
-        g = to_np(logits[b, torch.from_numpy(rows).cuda()])
-        check(f"logits[{b}] ({len(rows)} of the first {P} rows)", g, ol, wl.mode)
+    for b, P in ((0, wl.T), (3, 96)):
+        ol, opres = O.model_forward(ids[b:b + 1, :P], W, wl.h)
+        g = to_np(logits[b:b + 1, :P])
+        check(f"logits[{b}] (first {P} rows)", g, ol, wl.mode)
         check(f"cache[{b}] slots [0, {P})", to_np(cache[b:b + 1, ..., :P, :]), opres, wl.mode)
-        g_all.append(g)
-        o_all.append(ol)
-    tol, raw = argmax_agreement(np.concatenate(g_all), np.concatenate(o_all))
-    log(f"  argmax agreement tolerant {tol:.4f} raw {raw:.4f}")
-    assert tol >= 0.999
+        g_all.append(g[0])
+        o_all.append(ol[0])
+        del ol, opres
+    check_argmax(np.concatenate(g_all), np.concatenate(o_all), wl.mode, min_rows=1000)
     P = 192
     cache2 = new_cache(wl.mode, wl.B, wl.L, wl.h, P, wl.dh)
     logits2, st = run_forward(wl.mode, hp, Wd, np.ascontiguousarray(ids[:, :P]), cache=cache2, capacity=P)
@@ -254,7 +301,7 @@ def test_decode_matches_uncached(mode, V, n_ctx, d, h, L, B, T):
 
 def test_decode_gpt2s_full():
     """The decode workload at full size: 64 sequences at position 1023 with a
-    random past; sequences 0, 31 and 63 recomputed by the oracle."""
+    random past; every sequence recomputed by the oracle."""
     wl = WORKLOADS["gpt2s_decode_b64_p1023"]
     ids, W = model_inputs(wl)
     ids = ids[:, 0]
@@ -270,14 +317,17 @@ def test_decode_gpt2s_full():
     del past, bits
     step = run_decode(wl.mode, hp, Wd, ids, wl.l_past, cache, cap)
     g_all, o_all = [], []
-    for b in (0, 31, 63):
+    new_kv = to_np(cache[..., wl.l_past:wl.l_past + 1, :])
+    g_step = to_np(step)
+    errs, kv_errs = [], []
+    for b in range(wl.B):
         pb = past_for_sequence(wl, b)[None]
         ol, opres = O.decode_step(ids[b:b + 1], W, wl.h, past=pb)
-        g = to_np(step[b:b + 1])
-        check(f"logits[{b}]", g, ol, wl.mode)
-        check(f"new K/V[{b}]", to_np(cache[b:b + 1, ..., wl.l_past:wl.l_past + 1, :]), opres, wl.mode)
-        g_all.append(g[:, 0])
-        o_all.append(ol[:, 0])
-    tol, raw = argmax_agreement(np.concatenate(g_all), np.concatenate(o_all))
-    log(f"  argmax agreement tolerant {tol:.4f} raw {raw:.4f}")
-    assert tol >= 0.999
+        errs.append(float(np.abs(g_step[b:b + 1] - ol).max()))
+        kv_errs.append(float(np.abs(new_kv[b:b + 1] - opres).max()))
+        g_all.append(g_step[b])
+        o_all.append(ol[0])
+    log(f"  logits max abs err over {wl.B} sequences {max(errs):.3e}; new K/V {max(kv_errs):.3e}")
+    assert max(errs) <= TOL_BF16_ABS
+    assert max(kv_errs) <= TOL_BF16_ABS
+    check_argmax(np.concatenate(g_all), np.concatenate(o_all), wl.mode, min_rows=wl.B)

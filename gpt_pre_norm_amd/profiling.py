@@ -6,9 +6,9 @@ Commands (run from the repository root):
       One device-to-device copy of a known size; profile it with the same
       counters as the workload to get the scale from counter KiB to bytes.
 
-  python -m gpt_pre_norm_amd.profiling stats STATS_CSV OUT_TXT --command "..."
-      Per-kernel table (calls, average and total duration) from
-      rocprofv3 --kernel-trace --stats.
+  python -m gpt_pre_norm_amd.profiling stats STATS_CSV OUT_TXT --command "..." [--trace TRACE_CSV]
+      Per-kernel table (calls, average, median and total duration) from
+      rocprofv3 --kernel-trace --stats (the median from the kernel trace).
 
   python -m gpt_pre_norm_amd.profiling traffic --fetch CSV --write CSV
          --cal-fetch CSV --cal-write CSV --cal-mib N --out profiles/traffic.json
@@ -128,10 +128,23 @@ def cmd_calibrate(args):
 
 def cmd_stats(args):
     rows = list(csv.DictReader(open(args.csv)))
+    # per-kernel median launch duration from the kernel trace, when given:
+    # the average of the stats table also counts the first (cold) launches
+    med = {}
+    if args.trace:
+        durs = collections.defaultdict(list)
+        for r in csv.DictReader(open(args.trace)):
+            durs[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+        for name, d in durs.items():
+            d.sort()
+            med[name] = d[len(d) // 2] if len(d) % 2 else 0.5 * (d[len(d) // 2 - 1] + d[len(d) // 2])
     lines = [f"# rocprofv3 --kernel-trace --stats summary", f"# command: {args.command}", "#",
-             f"{'kernel':80s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_ms':>9s} {'pct':>6s}"]
+             f"{'kernel':80s} {'calls':>6s} {'avg_us':>10s} {'median_us':>10s} {'min_us':>10s} {'max_us':>10s} "
+             f"{'total_ms':>9s} {'pct':>6s}"]
     for r in rows:
+        m = med.get(r["Name"])
         lines.append(f"{short_name(r['Name'])[:80]:80s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{(f'{m:10.2f}' if m is not None else f'{chr(45):>10s}')} "
                      f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
                      f"{float(r['TotalDurationNs']) / 1e6:9.3f} {float(r['Percentage']):6.2f}")
     os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
@@ -233,6 +246,7 @@ def main(argv=None):
     s.add_argument("csv")
     s.add_argument("out")
     s.add_argument("--command", required=True)
+    s.add_argument("--trace", default=None, help="kernel_trace.csv of the same run (adds median_us)")
     t = sub.add_parser("traffic")
     for a in ("--fetch", "--write", "--cal-fetch", "--cal-write", "--out", "--command"):
         t.add_argument(a, required=True)

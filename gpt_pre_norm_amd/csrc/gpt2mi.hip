@@ -14,10 +14,16 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "../../include/gpt2mi.h"
 #include "kernels.h"
+
+// Workspace of gpt2_decode_step_noalloc: a file-scope device array that every
+// GPU the library runs on holds until the process ends (8 MiB).
+constexpr size_t kScratchBytes = 8u << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace {
 
@@ -152,6 +158,28 @@ gpt2_status check_common(const gpt2_hparams& hp, gpt2_mode mode, int B, int T, i
 }
 
 gpt2_status hip_status() { return hipGetLastError() == hipSuccess ? GPT2_OK : GPT2_E_HIP; }
+
+// ---------------------------------------------------------------- static scratch
+// The workspace of gpt2_decode_step_noalloc lives in `scratch` (defined above
+// the namespace).  In host code its name is only a stand-in for the symbol;
+// the device address, which differs per GPU, is looked up once per device and
+// kept, and only that address is ever passed to kernels.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch array on the current device (NULL on failure).
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
 
 // ---------------------------------------------------------------- kernel timing
 // Between gpt2_timing_begin and gpt2_timing_end every launch is bracketed by
@@ -385,20 +413,45 @@ gpt2_status gpt2_forward(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_weig
   return hip_status();
 }
 
-gpt2_status gpt2_decode_step(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_weights* W,
-                             const int32_t* ids, int32_t B, int32_t l_past, const gpt2_kv* cache,
-                             float* logits, void* ws, size_t ws_bytes, void* stream) {
+// Argument checks of the decode step, up to the workspace.
+gpt2_status decode_checks(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_weights* W, const int32_t* ids,
+                          int32_t B, int32_t l_past, const gpt2_kv* cache, float* logits) {
   gpt2_status st = check_hparams(hp, mode, true);
   if (st != GPT2_OK) return st;
   if (!ids || !logits || !cache) return GPT2_E_NULL;
   if (!cache->data) return GPT2_E_NULL;
   if ((st = check_weights(*hp, W)) != GPT2_OK) return st;
   if (!al4(ids) || !al4(logits) || !al16(cache->data)) return GPT2_E_ALIGN;
+  if (B < 1 || B > kMaxTokens) return GPT2_E_SHAPE;
+  if (l_past < 0 || (long long)l_past + 1 > hp->n_ctx || l_past >= cache->capacity) return GPT2_E_POSITION;
+  if (mode == GPT2_FP32 && l_past + 1 > kMaxRowKeysF32) return GPT2_E_SHAPE;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_decode_step(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_weights* W,
+                             const int32_t* ids, int32_t B, int32_t l_past, const gpt2_kv* cache,
+                             float* logits, void* ws, size_t ws_bytes, void* stream) {
+  gpt2_status st = decode_checks(hp, mode, W, ids, B, l_past, cache, logits);
+  if (st != GPT2_OK) return st;
   st = check_common(*hp, mode, B, 1, l_past, ws, ws_bytes);
   if (st != GPT2_OK) return st;
-  if (l_past >= cache->capacity) return GPT2_E_POSITION;
   (void)hipGetLastError();
   Run r{*hp, mode, B, 1, l_past, true, (char*)ws, layout(*hp, mode, B, 1), (hipStream_t)stream};
+  r.model(*W, ids, logits, cache);
+  return hip_status();
+}
+
+gpt2_status gpt2_decode_step_noalloc(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_weights* W,
+                                     const int32_t* ids, int32_t B, int32_t l_past, const gpt2_kv* cache,
+                                     float* logits, void* stream) {
+  gpt2_status st = decode_checks(hp, mode, W, ids, B, l_past, cache, logits);
+  if (st != GPT2_OK) return st;
+  const Layout L = layout(*hp, mode, B, 1);
+  if (L.total > kScratchBytes) return GPT2_E_WORKSPACE;
+  (void)hipGetLastError();
+  char* ws = (char*)scratch_on_current_device();
+  if (!ws) return GPT2_E_HIP;
+  Run r{*hp, mode, B, 1, l_past, true, ws, L, (hipStream_t)stream};
   r.model(*W, ids, logits, cache);
   return hip_status();
 }

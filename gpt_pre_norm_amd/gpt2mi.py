@@ -21,6 +21,7 @@ STATUS = {0: "GPT2_OK", 1: "GPT2_E_NULL", 2: "GPT2_E_SHAPE", 3: "GPT2_E_DTYPE",
           4: "GPT2_E_POSITION", 5: "GPT2_E_WORKSPACE", 6: "GPT2_E_TOKEN", 7: "GPT2_E_HIP",
           8: "GPT2_E_ALIGN"}
 EXPORTS = ("gpt2_workspace_size", "gpt2_block_forward", "gpt2_forward", "gpt2_prefill", "gpt2_decode_step",
+           "gpt2_decode_step_noalloc",
            "gpt2_generate_workspace_size", "gpt2_generate_greedy", "gpt2_loss_workspace_size",
            "gpt2_forward_loss", "gpt2_read_device_flags",
            "gpt2_timing_begin", "gpt2_timing_end", "gpt2_status_str")
@@ -79,6 +80,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                  ctypes.POINTER(KV), vp, vp, sz, vp]
     lib.gpt2_decode_step.argtypes = [hp_p, ctypes.c_int, ctypes.POINTER(Weights), vp, i32, i32,
                                      ctypes.POINTER(KV), vp, vp, sz, vp]
+    lib.gpt2_decode_step_noalloc.argtypes = [hp_p, ctypes.c_int, ctypes.POINTER(Weights), vp, i32, i32,
+                                             ctypes.POINTER(KV), vp, vp]
     lib.gpt2_generate_workspace_size.argtypes = [hp_p, ctypes.c_int, i32]
     lib.gpt2_generate_workspace_size.restype = sz
     lib.gpt2_generate_greedy.argtypes = [hp_p, ctypes.c_int, ctypes.POINTER(Weights), vp, i32, i32, i32,
@@ -94,7 +97,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gpt2_timing_end.restype = i32
     lib.gpt2_status_str.argtypes = [ctypes.c_int]
     lib.gpt2_status_str.restype = ctypes.c_char_p
-    for f in ("gpt2_block_forward", "gpt2_forward", "gpt2_prefill", "gpt2_decode_step", "gpt2_generate_greedy",
+    for f in ("gpt2_block_forward", "gpt2_forward", "gpt2_prefill", "gpt2_decode_step", "gpt2_decode_step_noalloc",
+              "gpt2_generate_greedy",
               "gpt2_forward_loss", "gpt2_read_device_flags"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
@@ -213,6 +217,14 @@ def decode_step(hp: HParams, mode: int, W: ModelWeights, ids, B: int, l_past: in
     _check(load().gpt2_decode_step(ctypes.byref(hp), mode, ctypes.byref(W.struct), _ptr(ids), B, l_past,
                                    ctypes.byref(kv), _ptr(logits), _ptr(ws), ws_bytes, _stream(stream)),
            "gpt2_decode_step")
+
+
+def decode_step_noalloc(hp: HParams, mode: int, W: ModelWeights, ids, B: int, l_past: int, cache, capacity: int,
+                        logits, stream=None):
+    kv = KV(_ptr(cache), capacity)
+    _check(load().gpt2_decode_step_noalloc(ctypes.byref(hp), mode, ctypes.byref(W.struct), _ptr(ids), B, l_past,
+                                           ctypes.byref(kv), _ptr(logits), _stream(stream)),
+           "gpt2_decode_step_noalloc")
 
 
 def generate_workspace(hp: HParams, mode: int, B: int, device="cuda") -> torch.Tensor:

@@ -139,6 +139,24 @@ gpt2_status gpt2_decode_step(const gpt2_hparams *hp, gpt2_mode mode, const gpt2_
                              const int32_t *ids, int32_t B, int32_t l_past, const gpt2_kv *cache,
                              float *logits, void *ws, size_t ws_bytes, void *stream);
 
+/* gpt2_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The step's intermediate buffers live in a
+ * fixed 8 MiB device array inside the library, one per GPU, held until the
+ * process ends; nothing is allocated or freed by the call.  A call whose
+ * workspace (gpt2_workspace_size(hp, mode, B, 1)) exceeds 8 MiB returns
+ * GPT2_E_WORKSPACE before anything is enqueued: in bf16 that is about
+ * 22 * B * n_embd bytes (B <= 64 at n_embd 2048, B <= 496 at 768), in fp32
+ * about 40 * B * n_embd.  Every call on a GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (other streams, other host threads) race
+ * and must be serialised by the caller.  An out-of-range token id zero-fills
+ * its row as in gpt2_decode_step, but its sticky flag lives in the library's
+ * array and is not reported (gpt2_read_device_flags reads a caller's
+ * workspace).  Other arguments, results and errors as gpt2_decode_step. */
+gpt2_status gpt2_decode_step_noalloc(const gpt2_hparams *hp, gpt2_mode mode, const gpt2_weights *W,
+                                     const int32_t *ids, int32_t B, int32_t l_past, const gpt2_kv *cache,
+                                     float *logits, void *stream);
+
 /* Forward over T new tokens per sequence against a cached past ("Full Forward
  * Pass", How it works: the model takes the past keys/values and new tokens, and
  * query t at position l_past + t attends to every key at positions

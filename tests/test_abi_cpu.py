@@ -119,6 +119,26 @@ def test_decode_and_forward_position_errors():
                             None) == 2
 
 
+def test_decode_noalloc_argument_errors():
+    """The no-alloc decode step checks its arguments like gpt2_decode_step and
+    refuses a batch whose workspace exceeds its fixed 8 MiB array, all before
+    anything touches a GPU."""
+    lib = G.load()
+    blocks = (G.BlockWeights * 2)(_block_weights(), _block_weights())
+    W = G.Weights(FAKE, FAKE, FAKE, FAKE, ctypes.cast(blocks, ctypes.POINTER(G.BlockWeights)))
+    kv = G.KV(FAKE, 1024)
+    hp = G.hparams(n_ctx=1024, n_layer=2)
+    call = lambda hp_, B, l_past, kv_=kv, ids=FAKE: lib.gpt2_decode_step_noalloc(
+        ctypes.byref(hp_), G.BF16, ctypes.byref(W), ids, B, l_past, ctypes.byref(kv_) if kv_ else None, FAKE, None)
+    assert call(hp, 4, 1024) == 4      # l_past + 1 beyond n_ctx
+    assert call(hp, 4, 5, kv_=None) == 1
+    assert call(hp, 0, 5) == 2
+    assert call(hp, 4, 5, ids=FAKE + 2) == 8
+    wide = G.hparams(n_ctx=1024, n_embd=2048, n_head=32, n_layer=2)
+    assert G.workspace_size(wide, G.BF16, 64, 1) <= 8 << 20 < G.workspace_size(wide, G.BF16, 200, 1)
+    assert call(wide, 200, 5) == 5     # beyond the fixed array
+
+
 def test_prefill_argument_errors():
     lib = G.load()
     hp = G.hparams(n_ctx=1024, n_layer=2)

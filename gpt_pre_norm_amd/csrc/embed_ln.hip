@@ -1,5 +1,6 @@
-// Embedding gather + position add fused with the first LayerNorm, and the
-// wave-per-row LayerNorm.
+// Embedding gather + position add fused with the first LayerNorm, the
+// wave-per-row LayerNorm, and the LayerNorm that first adds a residual
+// product kept as K-range partials (decode-sized calls).
 //
 // Embedding: H0 = wte[id] + wpe[l_past + t] ("Full Forward Pass", How it works).
 // LayerNorm: mean, biased variance of the deviations, (x - u) / sqrt(s + eps),
@@ -80,6 +81,75 @@ void launch_embed_ln(bool bf16, const int32_t* ids, const void* wte, const void*
     default: break;  // d <= 2048 is enforced by the caller
   }
 #undef GPT2_ELN_CASE
+}
+
+// The residual update of a product kept as K-range partials, then the
+// LayerNorm of the updated row: x = x + ((bias + p_0) + p_1 + ...) in range
+// order (the same order on every run), stored back, then a = LN(x).
+template <int NV>
+__global__ __launch_bounds__(64) void layernorm_reduce_kernel(float* __restrict__ x, const float* __restrict__ part,
+                                                              int S, long long sstride,
+                                                              const bf16_t* __restrict__ bias,
+                                                              const bf16_t* __restrict__ g,
+                                                              const bf16_t* __restrict__ b, bf16_t* __restrict__ a,
+                                                              int M, int d, float eps) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  if (row >= M) return;
+  float* xr = x + (long long)row * d;
+  const float* pr = part + (long long)row * d;
+  float4 v[NV];
+  // t = bias, then the partials added four ranges at a time: the four loads
+  // of a group are issued together (one memory round trip per group)
+  float4 t[NV], r[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = min((lane + 64 * i) * 4, d - 4);
+    t[i] = load4(bias + c);
+    r[i] = load4(xr + c);
+  }
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    float4 u[4][NV];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int c = min((lane + 64 * i) * 4, d - 4);
+        u[j][i] = s0 + j < S ? load4(pr + (s0 + j) * sstride + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (s0 + j < S)
+          t[i] = make_float4(t[i].x + u[j][i].x, t[i].y + u[j][i].y, t[i].z + u[j][i].z, t[i].w + u[j][i].w);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = (lane + 64 * i) * 4;
+    v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < d) {
+      v[i] = make_float4(r[i].x + t[i].x, r[i].y + t[i].y, r[i].z + t[i].z, r[i].w + t[i].w);
+      store4(xr + c, v[i]);
+    }
+  }
+  ln_row_regs<NV>(v, g, b, a + (long long)row * d, d, eps, lane);
+}
+
+void launch_layernorm_reduce(float* x, const float* part, int S, const void* bias, const void* g, const void* b,
+                             void* a, int M, int d, float eps, hipStream_t s) {
+  const int nv = (d + 255) / 256;
+  const long long ss = (long long)M * d;
+#define GPT2_LNR_CASE(N)                                                                                 \
+  case N:                                                                                                \
+    layernorm_reduce_kernel<N><<<M, 64, 0, s>>>(x, part, S, ss, (const bf16_t*)bias, (const bf16_t*)g,   \
+                                                (const bf16_t*)b, (bf16_t*)a, M, d, eps);                \
+    break;
+  switch (nv) {
+    GPT2_LNR_CASE(1) GPT2_LNR_CASE(2) GPT2_LNR_CASE(3) GPT2_LNR_CASE(4)
+    GPT2_LNR_CASE(5) GPT2_LNR_CASE(6) GPT2_LNR_CASE(7) GPT2_LNR_CASE(8)
+    default: break;  // d <= 2048 is enforced by the caller
+  }
+#undef GPT2_LNR_CASE
 }
 
 template <typename Tin, typename Tact>

@@ -12,7 +12,8 @@
 //     v_mfma_f32_32x32x16_bf16, tiles DMA'd global -> LDS with
 //     global_load_lds_dwordx4 through a two-stage ring, epilogue through a
 //     per-wave LDS patch so stores cover whole rows of 128 bytes;
-//   * M <= 64 (decode): a weight-streaming kernel with split K;
+//   * M <= 64 (decode): a weight-streaming kernel (split K into fixed-order
+//     partials for the in-place residual products);
 //   * otherwise: a register-staged 16x16x32 kernel.
 // fp32 path: a plain LDS-tiled FMA kernel (correctness mode).
 #include "kernels.h"
@@ -163,12 +164,9 @@ struct EpiBiasResid {
   GPT2_DEV void operator()(int m, int n, f32x4_t v) const { store(m, n, v, load(m, n)); }
 };
 
-// In-place fp32 residual update x += acc + bias.  The skinny decode kernel may
-// split K over workgroups; it then calls add(), which accumulates each K
-// range's share with fp32 atomics and adds the bias once (first range).
+// In-place fp32 residual update x += acc + bias.
 template <typename Tact>
 struct EpiResidInPlace {
-  static constexpr bool kAtomicResid = true;
   const Tact* bias;
   float* x;
   int N;
@@ -185,14 +183,24 @@ struct EpiResidInPlace {
         make_float4(c.r.x + (v[0] + b.x), c.r.y + (v[1] + b.y), c.r.z + (v[2] + b.z), c.r.w + (v[3] + b.w));
   }
   GPT2_DEV void operator()(int m, int n, f32x4_t v) const { store(m, n, v, load(m, n)); }
-  GPT2_DEV void add(int m, int n, f32x4_t v, bool with_bias) const {
-    float* p = x + (long long)m * N + n;
-    float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (with_bias) b = load4(bias + n);
-    unsafeAtomicAdd(p + 0, v[0] + b.x);
-    unsafeAtomicAdd(p + 1, v[1] + b.y);
-    unsafeAtomicAdd(p + 2, v[2] + b.z);
-    unsafeAtomicAdd(p + 3, v[3] + b.w);
+};
+
+// The products of S ranges of K, kept apart for a fixed-order sum later:
+// part[split][m][n] (fp32, [S][M][N]).  The skinny decode kernel writes
+// them when an in-place residual product splits K over workgroups; the
+// LayerNorm that follows adds them to the residual stream in range order
+// (launch_layernorm_reduce), so results do not depend on timing.
+struct EpiPartial {
+  static constexpr bool kPartial = true;
+  float* part;
+  int N;
+  long long split_stride;  // M * N
+  struct Ctx {};
+  GPT2_DEV Ctx load(int, int) const { return {}; }
+  GPT2_DEV void store(int, int, f32x4_t, Ctx) const {}
+  GPT2_DEV void operator()(int, int, f32x4_t) const {}
+  GPT2_DEV void put(int split, int m, int n, f32x4_t v) const {
+    *reinterpret_cast<f32x4_t*>(part + split * split_stride + (long long)m * N + n) = v;
   }
 };
 
@@ -773,14 +781,14 @@ static void run_bf16_v3(const bf16_t* X, const bf16_t* W, int M, int N, int K, c
 // at once with global_load_lds_dwordx4 (coalesced rows, XOR-swizzled 16-byte
 // chunks in LDS), waits once, and its 4 waves split kc for the MFMA
 // v_mfma_f32_16x16x32_bf16 (W rows as the A operand).  The waves' partial sums
-// meet in LDS.  S > 1 is used only for the in-place fp32 residual epilogue,
-// which then adds each K range's share with fp32 atomics (the bias with the
-// first range); every other epilogue runs with S = 1.
+// meet in LDS.  S > 1 is used only with EpiPartial, which keeps each K
+// range's product apart for a fixed-order sum; every other epilogue runs
+// with S = 1.
 constexpr int kSkinnyMaxKc = 768;
 
 template <class Epi>
-constexpr bool atomic_resid() {
-  if constexpr (requires { Epi::kAtomicResid; }) return Epi::kAtomicResid;
+constexpr bool partial_out() {
+  if constexpr (requires { Epi::kPartial; }) return Epi::kPartial;
   else return false;
 }
 
@@ -861,23 +869,21 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16_t* __restri
     const int m = 16 * (f & 3) + l16;
     const int n = n0 + 16 * (f >> 2) + 4 * kg;
     if (m < M && n < N) {
-      if constexpr (atomic_resid<Epi>()) {
-        if (S > 1) {
-          epi.add(m, n, f32x4_t{v.x, v.y, v.z, v.w}, split == 0);
-          continue;
-        }
-      }
-      epi(m, n, f32x4_t{v.x, v.y, v.z, v.w});
+      if constexpr (partial_out<Epi>())
+        epi.put(split, m, n, f32x4_t{v.x, v.y, v.z, v.w});
+      else
+        epi(m, n, f32x4_t{v.x, v.y, v.z, v.w});
     }
   }
 }
 
 // K ranges for the skinny kernel: the fewest that keep kc = K/S <= 768 with
-// K/S a multiple of 128 (16 chunks per LDS row) and, where the epilogue can
-// take K ranges (min_wg > 0), give at least min_wg workgroups over the
-// nslices column slices.  Each range adds its M x N fp32 atomics, so no more
-// than that: at M = 64, N = K = 768 (48 slices) two ranges took 4.5 us
-// against 5.3 us for one and 6.7 us for six.  0 if none exists.
+// K/S a multiple of 128 (16 chunks per LDS row) and, where the products may
+// be kept per range (min_wg > 0), give at least min_wg workgroups over the
+// nslices column slices.  Each range adds an M x N fp32 partial to write
+// and sum, so no more than that: at M = 64, N = K = 768 (48 slices) two
+// ranges took 4.5 us against 5.3 us for one and 6.7 us for six.  0 if none
+// exists.
 static int skinny_splits(int K, int nslices = 0, int min_wg = 0) {
   int first = 0;
   for (int s = 1; s <= K / 128; ++s)
@@ -910,9 +916,8 @@ template <class Epi>
 static bool try_skinny(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
                        hipStream_t s) {
   if (M > 64) return false;
-  const int nslices = N >= 8192 ? (N + 31) / 32 : (N + 15) / 16;
-  const int S = atomic_resid<Epi>() ? skinny_splits(K, nslices, 96) : skinny_splits(K);
-  if (S == 0 || (S > 1 && !atomic_resid<Epi>())) return false;
+  const int S = skinny_splits(K);
+  if (S != 1) return false;
   if (N >= 8192)
     run_skinny<32>(X, W, M, N, K, S, epi, s);
   else
@@ -1074,6 +1079,16 @@ static void launch_typed(const Tact* X, const Tact* W, int M, int N, int K, cons
                       FastDiv::make(e.T), FastDiv::make(e.d_head)});
       break;
   }
+}
+
+int residual_splits(bool bf16, int M, int N, int K) {
+  if (!bf16 || M > 64 || N >= 8192 || N % 8 != 0) return 1;
+  const int S = skinny_splits(K, (N + 15) / 16, 96);
+  return S > 1 ? S : 1;
+}
+
+void launch_gemm_partials(const void* X, const void* W, int M, int N, int K, int S, float* part, hipStream_t s) {
+  run_skinny<16>((const bf16_t*)X, (const bf16_t*)W, M, N, K, S, EpiPartial{part, N, (long long)M * N}, s);
 }
 
 bool head_lse_fused(bool bf16, int M, int K) { return bf16 && M > 64 && K % 64 == 0; }

@@ -13,6 +13,7 @@
 
 #include <cmath>
 #include <cstddef>
+#include <algorithm>
 #include <cstdint>
 #include <mutex>
 #include <vector>
@@ -21,8 +22,8 @@
 #include "kernels.h"
 
 // Workspace of gpt2_decode_step_noalloc: a file-scope device array that every
-// GPU the library runs on holds until the process ends (8 MiB).
-constexpr size_t kScratchBytes = 8u << 20;
+// GPU the library runs on holds until the process ends (16 MiB).
+constexpr size_t kScratchBytes = 16u << 20;
 static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace {
@@ -47,14 +48,28 @@ bool al16(const void* p) { return (uintptr_t)p % 16 == 0; }
 bool al4(const void* p) { return (uintptr_t)p % 4 == 0; }
 
 struct Layout {
-  size_t x, a, q, o, u, kv, total;
+  size_t x, a, q, o, u, kv, part, total;
 };
 
+// K ranges of the block's two residual products (attention c_proj, mlp
+// c_proj) when they are split for a decode-sized call (1: not split).
+int proj_splits(const gpt2_hparams& hp, gpt2_mode mode, int M) {
+  const int d = hp.n_embd;
+  return residual_splits(mode == GPT2_BF16, M, d, d);
+}
+int fc2_splits(const gpt2_hparams& hp, gpt2_mode mode, int M) {
+  const int d = hp.n_embd;
+  return residual_splits(mode == GPT2_BF16, M, d, 4 * d);
+}
+
 // Workspace regions for M = B*T rows: fp32 residual x, LN output a, q, attention
-// output o, MLP hidden u and K/V scratch (when no present/cache is given).
+// output o, MLP hidden u, K/V scratch (when no present/cache is given) and,
+// for decode-sized calls, the K-range partials of the residual products.
 Layout layout(const gpt2_hparams& hp, gpt2_mode mode, int B, int T) {
   const size_t act = mode == GPT2_BF16 ? 2 : 4;
   const size_t M = (size_t)B * T, d = (size_t)hp.n_embd;
+  const int m = (int)std::min(M, (size_t)kMaxTokens);
+  const size_t S = (size_t)std::max(proj_splits(hp, mode, m), fc2_splits(hp, mode, m));
   Layout L;
   size_t off = kHeader;
   L.x = off;  off += up(M * d * 4);
@@ -63,6 +78,7 @@ Layout layout(const gpt2_hparams& hp, gpt2_mode mode, int B, int T) {
   L.o = off;  off += up(M * d * act);
   L.u = off;  off += up(M * 4 * d * act);
   L.kv = off; off += up(2 * M * d * act);
+  L.part = off; off += S > 1 ? up(S * M * d * 4) : 0;
   L.total = off;
   return L;
 }
@@ -243,17 +259,31 @@ struct Run {
 
   // One pre-norm block.  x_in: block input (fp32 if x_in_f32, else act dtype);
   // x1: fp32 stream after the attention residual; y: block output.
-  // ln1_done: a already holds LN1(x_in).
-  void block(const gpt2_block_weights& w, const void* x_in, bool x_in_f32, float* x1, void* y,
-             bool y_f32, KvView kv, bool ln1_done = false) const {
+  // ln1_done: a already holds LN1(x_in).  pend_S > 0: x_in (the fp32 stream,
+  // updated in place) still lacks the previous block's mlp c_proj, held as
+  // pend_S K-range partials whose bias is pend_bias; LN1 adds them first.
+  // Returns the count of K-range partials this block's own mlp c_proj left
+  // pending in the same way (0: its output is complete).
+  int block(const gpt2_block_weights& w, const void* x_in, bool x_in_f32, float* x1, void* y, bool y_f32,
+            KvView kv, bool ln1_done = false, const void* pend_bias = nullptr, int pend_S = 0) const {
     const int d = hp.n_embd, H = hp.n_head, dh = d / H, m = M();
     const bool b16 = bf16();
     void* a = at(L.a);
     void* q = at(L.q);
     void* o = at(L.o);
     void* u = at(L.u);
+    float* part = (float*)at(L.part);
+    // the residual products update the fp32 stream in place: decode-sized
+    // ones may be split into K-range partials
+    const bool in_place = x_in_f32 && x_in == (const void*)x1 && (void*)x1 == y && y_f32;
+    const int s_proj = in_place ? proj_splits(hp, mode, m) : 1;
+    const int s_fc2 = in_place ? fc2_splits(hp, mode, m) : 1;
     // LN1
-    if (!ln1_done)
+    if (pend_S > 0)
+      timed(K_LAYERNORM, s, [&] {
+        launch_layernorm_reduce(x1, part, pend_S, pend_bias, w.ln1_g, w.ln1_b, a, m, d, hp.eps, s);
+      });
+    else if (!ln1_done)
       timed(K_LAYERNORM, s, [&] { launch_layernorm(x_in_f32 || !b16, b16, x_in, w.ln1_g, w.ln1_b, a, m, d, hp.eps, s); });
     // c_attn: q to [B,H,T,dh], k/v into the view at positions l_past..
     Epilogue e{};
@@ -276,23 +306,34 @@ struct Run {
     } else {
       timed(K_ATTN_PREFILL, s, [&] { launch_attn_prefill_bf16((const bf16_t*)q, kv, (bf16_t*)o, B, H, T, l_past, s); });
     }
-    // c_proj + bias + residual -> x1 (fp32)
-    Epilogue p{};
-    p.kind = EPI_BIAS_RESID;
-    p.bias = w.proj_b;
-    p.resid = x_in;
-    p.resid_f32 = x_in_f32 || !b16;
-    p.out = x1;
-    p.out_f32 = true;
-    timed(K_GEMM_ATTN_PROJ, s, [&] { launch_gemm(b16, o, w.proj_w, m, d, d, p, s); });
-    // LN2, c_fc + GELU
-    timed(K_LAYERNORM, s, [&] { launch_layernorm(true, b16, x1, w.ln2_g, w.ln2_b, a, m, d, hp.eps, s); });
+    // c_proj + bias + residual -> x1 (fp32), then LN2
+    if (s_proj > 1) {
+      timed(K_GEMM_ATTN_PROJ, s, [&] { launch_gemm_partials(o, w.proj_w, m, d, d, s_proj, part, s); });
+      timed(K_LAYERNORM, s, [&] {
+        launch_layernorm_reduce(x1, part, s_proj, w.proj_b, w.ln2_g, w.ln2_b, a, m, d, hp.eps, s);
+      });
+    } else {
+      Epilogue p{};
+      p.kind = EPI_BIAS_RESID;
+      p.bias = w.proj_b;
+      p.resid = x_in;
+      p.resid_f32 = x_in_f32 || !b16;
+      p.out = x1;
+      p.out_f32 = true;
+      timed(K_GEMM_ATTN_PROJ, s, [&] { launch_gemm(b16, o, w.proj_w, m, d, d, p, s); });
+      timed(K_LAYERNORM, s, [&] { launch_layernorm(true, b16, x1, w.ln2_g, w.ln2_b, a, m, d, hp.eps, s); });
+    }
+    // c_fc + GELU
     Epilogue f{};
     f.kind = EPI_BIAS_GELU;
     f.bias = w.fc_b;
     f.out = u;
     timed(K_GEMM_C_FC, s, [&] { launch_gemm(b16, a, w.fc_w, m, 4 * d, d, f, s); });
-    // mlp.c_proj + bias + residual -> y
+    // mlp.c_proj + bias + residual -> y (left as partials for the next LayerNorm when split)
+    if (s_fc2 > 1) {
+      timed(K_GEMM_MLP_PROJ, s, [&] { launch_gemm_partials(u, w.fc2_w, m, d, 4 * d, s_fc2, part, s); });
+      return s_fc2;
+    }
     Epilogue f2{};
     f2.kind = EPI_BIAS_RESID;
     f2.bias = w.fc2_b;
@@ -301,6 +342,7 @@ struct Run {
     f2.out = y;
     f2.out_f32 = y_f32 || !b16;
     timed(K_GEMM_MLP_PROJ, s, [&] { launch_gemm(b16, u, w.fc2_w, m, d, 4 * d, f2, s); });
+    return 0;
   }
 
   // Cache [B, n_layer, 2, H, cap, dh] viewed at one layer.
@@ -345,11 +387,19 @@ struct Run {
       launch_embed_ln(b16, ids, W.wte, W.wpe, x, W.blocks[0].ln1_g, W.blocks[0].ln1_b, a, m, T, l_past, d,
                       hp.n_vocab, hp.eps, (uint32_t*)ws, s);
     });
+    int pend = 0;  // K-range partials of the previous block's mlp c_proj not yet added
     for (int l = 0; l < hp.n_layer; ++l) {
       const KvView kv = cache ? cache_view(cache->data, cache->capacity, l) : present_view(at(L.kv));
-      block(W.blocks[l], x, true, x, x, true, kv, l == 0);
+      pend = block(W.blocks[l], x, true, x, x, true, kv, l == 0, l > 0 ? W.blocks[l - 1].fc2_b : nullptr, pend);
     }
-    timed(K_LAYERNORM, s, [&] { launch_layernorm(true, b16, x, W.lnf_g, W.lnf_b, a, m, d, hp.eps, s); });
+    if (pend > 0) {
+      const void* bias = W.blocks[hp.n_layer - 1].fc2_b;
+      timed(K_LAYERNORM, s, [&] {
+        launch_layernorm_reduce(x, (const float*)at(L.part), pend, bias, W.lnf_g, W.lnf_b, a, m, d, hp.eps, s);
+      });
+    } else {
+      timed(K_LAYERNORM, s, [&] { launch_layernorm(true, b16, x, W.lnf_g, W.lnf_b, a, m, d, hp.eps, s); });
+    }
   }
 };
 

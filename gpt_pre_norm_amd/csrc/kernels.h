@@ -24,6 +24,13 @@ void launch_embed_ln(bool bf16, const int32_t* ids, const void* wte, const void*
 void launch_layernorm(bool x_f32, bool act_bf16, const void* x, const void* g, const void* b,
                       void* y, int M, int d, float eps, hipStream_t s);
 
+// Residual update and LayerNorm for products kept as K-range partials
+// (bf16 activations, fp32 stream): x[m] <- x[m] + ((bias + part[0][m]) +
+// part[1][m] + ... + part[S-1][m]), a fixed order; then a = LN(x) as
+// launch_layernorm.  part is [S][M][d] fp32.
+void launch_layernorm_reduce(float* x, const float* part, int S, const void* bias, const void* g, const void* b,
+                             void* a, int M, int d, float eps, hipStream_t s);
+
 // ---------------------------------------------------------------- GEMM
 enum EpiKind {
   EPI_STORE_F32 = 0,   // out fp32 [M, N] = acc                    (tied head)
@@ -48,10 +55,17 @@ struct Epilogue {
 
 // Y = X W^T with the epilogue; X [M, K], W [N, K] row-major.
 // bf16: MFMA paths (K % 8 == 0; M <= 64 uses the weight-streaming skinny
-// kernel when K allows); else fp32 FMA path (K % 4 == 0).  An in-place fp32
-// residual update (resid == out) may be accumulated with fp32 atomics.
+// kernel when K allows); else fp32 FMA path (K % 4 == 0).
 void launch_gemm(bool bf16, const void* X, const void* W, int M, int N, int K, const Epilogue& e,
                  hipStream_t s);
+
+// Decode-sized in-place residual products (bf16, M <= 64) stream their
+// weights faster over more workgroups when K is split into ranges: the
+// number of ranges S for X [M, K] x W [N, K]^T, or 1 when the product is not
+// split.  launch_gemm_partials then writes the S range products to part
+// [S][M][N] fp32 (no bias); launch_layernorm_reduce adds them up.
+int residual_splits(bool bf16, int M, int N, int K);
+void launch_gemm_partials(const void* X, const void* W, int M, int N, int K, int S, float* part, hipStream_t s);
 
 // ---------------------------------------------------------------- head + cross-entropy
 // Fused tied head for the loss (bf16, M > 64, K % 64 == 0): logits of X [M, K]

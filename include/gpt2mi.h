@@ -35,11 +35,10 @@
  *     embedding kernel zero-fills that row and raises a sticky device flag in
  *     the workspace that gpt2_read_device_flags reports and clears.
  *   - Concurrent calls must use distinct workspaces.
- *   - Reproducibility (GPT2_BF16): with B*T > 64 rows a call is deterministic,
- *     bit for bit.  With B*T <= 64 (the decode step, greedy generation) the
- *     residual products split their K range over workgroups and add the parts
- *     with fp32 atomics in no fixed order, so results may differ in the last
- *     bits between runs.
+ *   - Reproducibility: every call is deterministic, bit for bit, for given
+ *     inputs and sizes.  (With B*T <= 64 rows in GPT2_BF16 the residual
+ *     products split their K range over workgroups; the parts are added in a
+ *     fixed order by the LayerNorm that follows.)
  *   - Device pointers to weights, activations and the K/V cache must be
  *     16-byte aligned; token ids, targets, outputs of ids and fp32 logits /
  *     losses 4-byte aligned; the workspace 256-byte aligned (any hipMalloc or
@@ -142,12 +141,12 @@ gpt2_status gpt2_decode_step(const gpt2_hparams *hp, gpt2_mode mode, const gpt2_
 /* gpt2_decode_step without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  The step's intermediate buffers live in a
- * fixed 8 MiB device array inside the library, one per GPU, held until the
+ * fixed 16 MiB device array inside the library, one per GPU, held until the
  * process ends; nothing is allocated or freed by the call.  A call whose
- * workspace (gpt2_workspace_size(hp, mode, B, 1)) exceeds 8 MiB returns
- * GPT2_E_WORKSPACE before anything is enqueued: in bf16 that is about
- * 22 * B * n_embd bytes (B <= 64 at n_embd 2048, B <= 496 at 768), in fp32
- * about 40 * B * n_embd.  Every call on a GPU shares that GPU's array: calls
+ * workspace (gpt2_workspace_size(hp, mode, B, 1)) exceeds 16 MiB returns
+ * GPT2_E_WORKSPACE before anything is enqueued (in bf16 that admits every
+ * B <= 64 up to n_embd 2048 and, at n_embd 768, B up to 992; in fp32 about
+ * 40 * B * n_embd bytes are needed).  Every call on a GPU shares that GPU's array: calls
  * that overlap in time on one GPU (other streams, other host threads) race
  * and must be serialised by the caller.  An out-of-range token id zero-fills
  * its row as in gpt2_decode_step, but its sticky flag lives in the library's

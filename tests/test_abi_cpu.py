@@ -121,7 +121,7 @@ def test_decode_and_forward_position_errors():
 
 def test_decode_noalloc_argument_errors():
     """The no-alloc decode step checks its arguments like gpt2_decode_step and
-    refuses a batch whose workspace exceeds its fixed 8 MiB array, all before
+    refuses a batch whose workspace exceeds its fixed 16 MiB array, all before
     anything touches a GPU."""
     lib = G.load()
     blocks = (G.BlockWeights * 2)(_block_weights(), _block_weights())
@@ -135,8 +135,8 @@ def test_decode_noalloc_argument_errors():
     assert call(hp, 0, 5) == 2
     assert call(hp, 4, 5, ids=FAKE + 2) == 8
     wide = G.hparams(n_ctx=1024, n_embd=2048, n_head=32, n_layer=2)
-    assert G.workspace_size(wide, G.BF16, 64, 1) <= 8 << 20 < G.workspace_size(wide, G.BF16, 200, 1)
-    assert call(wide, 200, 5) == 5     # beyond the fixed array
+    assert G.workspace_size(wide, G.BF16, 64, 1) <= 16 << 20 < G.workspace_size(wide, G.BF16, 400, 1)
+    assert call(wide, 400, 5) == 5     # beyond the fixed array
 
 
 def test_prefill_argument_errors():

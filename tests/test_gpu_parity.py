@@ -299,6 +299,28 @@ def test_decode_matches_uncached(mode, V, n_ctx, d, h, L, B, T):
     check("cache slots < l_past", to_np(cache)[..., :T, :], opres, mode)
 
 
+def test_decode_bit_reproducible():
+    """Decode-sized calls split the residual products' K range over
+    workgroups; the parts are added in a fixed order, so two runs of the same
+    step on the same inputs give the same bits (logits and cache slot)."""
+    V, n_ctx, d, h, L, B, T = 1001, 128, 768, 12, 2, 64, 40
+    W, Wd, hp = _small_model(G.BF16, V, n_ctx, d, h, L, 760)
+    ids = synth.ids_input((B, T), V, 761)
+    cache = new_cache(G.BF16, B, L, h, n_ctx, d // h)
+    _, st = run_forward(G.BF16, hp, Wd, ids[:, :T - 1], cache=cache, capacity=n_ctx)
+    assert st == 0
+    outs = []
+    for _ in range(3):
+        c = cache.clone()
+        logits = run_decode(G.BF16, hp, Wd, ids[:, T - 1], T - 1, c, n_ctx)
+        outs.append((logits.clone(), c[..., T - 1, :].clone()))
+    for lg, kv in outs[1:]:
+        assert torch.equal(lg, outs[0][0])
+        assert torch.equal(kv, outs[0][1])
+    ol, _ = O.model_forward(ids, W, h, logit_rows=np.arange(B) * T + T - 1)
+    check("logits", to_np(outs[0][0])[:, 0], ol, G.BF16)
+
+
 def test_decode_gpt2s_full():
     """The decode workload at full size: 64 sequences at position 1023 with a
     random past; every sequence recomputed by the oracle."""

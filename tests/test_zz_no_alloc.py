@@ -8,7 +8,7 @@ import torch
 
 from gpt_pre_norm_amd import gpt2mi as G
 from gpt_pre_norm_amd import synth
-from tests.gpu_helpers import TOL_BF16_ABS, hp_of, log, new_cache, run_forward, to_np
+from tests.gpu_helpers import hp_of, log, new_cache, run_forward, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -52,24 +52,19 @@ def test_noalloc_matches_workspace_step(mode):
         assert st == 0
         (lw, kvw), (ln, kvn) = _decode_both(mode, hp, Wd, ids[:, T - 1], T - 1, cache, n_ctx)
         assert np.isfinite(ln).all()
-        if mode == G.FP32:
-            # no atomics in the fp32 products: the same kernels give the same bits
-            log(f"  fp32 B={B}: logits identical {np.array_equal(lw, ln)}")
-            assert np.array_equal(lw, ln)
-            assert np.array_equal(kvw, kvn)
-        else:
-            # bf16 decode adds K ranges with fp32 atomics in no fixed order
-            err = float(np.abs(lw - ln).max())
-            kerr = float(np.abs(kvw - kvn).max())
-            log(f"  bf16 B={B}: logits max abs diff {err:.3e}, new K/V {kerr:.3e}")
-            assert err <= TOL_BF16_ABS and kerr <= TOL_BF16_ABS
+        # the same kernels in the same order on the same inputs: the same bits
+        # (the decode step adds its K-range partials in a fixed order)
+        log(f"  mode={mode} B={B}: logits identical {np.array_equal(lw, ln)}, "
+            f"max abs diff {float(np.abs(lw - ln).max()):.3e}")
+        assert np.array_equal(lw, ln)
+        assert np.array_equal(kvw, kvn)
 
 
 def test_noalloc_rejects_oversized_batch():
     V, d, h, L = 301, 2048, 32, 1
     W = synth.model_weights(V, 16, d, L, 1310, bf16=True)
     Wd, hp = G.upload_model(W, G.BF16), hp_of(V, 16, d, h, L)
-    B = 200  # about 9 MB of workspace at n_embd 2048, over the 8 MiB array
+    B = 400  # about 18 MB of workspace at n_embd 2048, over the 16 MiB array
     ids = torch.zeros(B, dtype=torch.int32, device="cuda")
     cache = new_cache(G.BF16, B, L, h, 16, d // h)
     logits = torch.empty((B, 1, V), dtype=torch.float32, device="cuda")

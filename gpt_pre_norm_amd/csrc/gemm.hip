@@ -84,17 +84,25 @@ struct EpiStoreF32Lines {
   struct Ctx {};
   GPT2_DEV Ctx load(int, int) const { return {}; }
   GPT2_DEV void store(int i, int n, f32x4_t v, Ctx) const { (*this)(i, n, v); }
+  GPT2_DEV void operator()(int i, int n, f32x4_t v) const { store(row(i), n, v, Ctx{}); }
+  // The row of position i is found once per row a lane stores, not per
+  // store (kColRow): it takes integer divisions.
+  static constexpr bool kColRow = true;
+  using Col = int;
+  using Row = long long;  // row_of(i) * N
+  GPT2_DEV Col col(int n) const { return n; }
+  GPT2_DEV Row row(int i) const { return (long long)row_of(i) * N; }
   // Non-temporal stores: the logits are not read back by this kernel, and
   // kept out of the way in L2 they leave it to the X and W tiles that every
   // workgroup re-reads.
-  GPT2_DEV void operator()(int i, int n, f32x4_t v) const {
-    float* p = out + (long long)row_of(i) * N + n;
+  GPT2_DEV void store(Row r, Col n, f32x4_t v, Ctx) const {
+    float* p = out + r + n;
     if (n >= 0 && n + 3 < N) {
       __builtin_nontemporal_store(v, reinterpret_cast<f32x4u_t*>(p));
     } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (n + r >= 0 && n + r < N) __builtin_nontemporal_store(v[r], p + r);
+      for (int k = 0; k < 4; ++k)
+        if (n + k >= 0 && n + k < N) __builtin_nontemporal_store(v[k], p + k);
     }
   }
 };
@@ -214,23 +222,38 @@ struct EpiQKV {
   using Ctx = typename Raw4<Tact>::type;  // bias
   GPT2_DEV Ctx load(int, int n) const { return load4_raw(bias + n); }
   GPT2_DEV void operator()(int m, int n, f32x4_t v) const { store(m, n, v, load(m, n)); }
-  GPT2_DEV void store(int m, int n, f32x4_t v, const Ctx& braw) const {
-    const float4 b = widen4(braw);
-    const float4 y = make_float4(v[0] + b.x, v[1] + b.y, v[2] + b.z, v[3] + b.w);
+  // The destination splits into a part that depends on the column only (q,
+  // k or v; head; element) and one that depends on the row only (sequence,
+  // position), so the tile epilogue computes each once per column block
+  // and per row rather than per store (kColRow).
+  static constexpr bool kColRow = true;
+  struct Col {
+    bool is_q;
+    long long off;  // elements from q (is_q) or from the K/V view base
+  };
+  struct Row {
+    long long q_off, kv_off;
+  };
+  GPT2_DEV Col col(int n) const {
     const int sec = (n >= d) + (n >= 2 * d);
     const int c = n - sec * d;
     const int h = (int)divDh.div((uint32_t)c);
     const int j = c - h * dh;
+    if (sec == 0) return {true, (long long)h * T * dh + j};
+    return {false, (sec - 1) * kv.skv + h * kv.sh + (long long)l_past * dh + j};
+  }
+  GPT2_DEV Row row(int m) const {
     const int bi = (int)divT.div((uint32_t)m);
     const int t = m - bi * T;
-    Tact* dst;
-    if (sec == 0)
-      dst = q + (((long long)bi * H + h) * T + t) * dh + j;
-    else
-      dst = (Tact*)kv.base + bi * kv.sb + (sec - 1) * kv.skv + h * kv.sh +
-            (long long)(l_past + t) * dh + j;
+    return {((long long)bi * H * T + t) * dh, bi * kv.sb + (long long)t * dh};
+  }
+  GPT2_DEV void store(const Row& r, const Col& c, f32x4_t v, const Ctx& braw) const {
+    const float4 b = widen4(braw);
+    const float4 y = make_float4(v[0] + b.x, v[1] + b.y, v[2] + b.z, v[3] + b.w);
+    Tact* dst = c.is_q ? q + (c.off + r.q_off) : (Tact*)kv.base + (c.off + r.kv_off);
     store4(dst, y);
   }
+  GPT2_DEV void store(int m, int n, f32x4_t v, const Ctx& braw) const { store(row(m), col(n), v, braw); }
 };
 
 // ================================================================ tile order
@@ -564,6 +587,32 @@ GPT2_DEV void tile_epilogue_loads(typename Epi::Ctx (&cx)[FN][FM][4], const Epi&
   }
 }
 
+template <class Epi>
+constexpr bool col_row() {
+  if constexpr (requires { Epi::kColRow; }) return Epi::kColRow;
+  else return false;
+}
+
+// Per-row part of a kColRow epilogue's destinations, one per row a lane
+// stores (or an empty placeholder for other epilogues).
+template <class Epi, bool = col_row<Epi>()>
+struct RowParts {
+  template <int FM>
+  GPT2_DEV void init(const Epi&, int, int, int) {}
+};
+template <class Epi>
+struct RowParts<Epi, true> {
+  typename Epi::Row r[4 * 4];  // up to FM = 4 fragments x 4 rows
+  template <int FM>
+  GPT2_DEV void init(const Epi& epi, int M, int mw0, int er) {
+    static_assert(FM <= 4, "row parts");
+#pragma unroll
+    for (int b = 0; b < FM; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[b * 4 + i] = epi.row(min(mw0 + b * 32 + 8 * i + er, M - 1));
+  }
+};
+
 template <int FM, int FN, class Epi>
 GPT2_DEV void tile_epilogue(const f32x16_t (&acc)[FN][FM], const typename Epi::Ctx (&cx)[FN][FM][4], uint4* lds,
                             const Epi& epi, int M, int N, int mw0, int nw0, int wave, int lane) {
@@ -571,6 +620,8 @@ GPT2_DEV void tile_epilogue(const f32x16_t (&acc)[FN][FM], const typename Epi::C
   float* patch = reinterpret_cast<float*>(lds) + wave * (32 * 36);
   const int er = lane >> 3;        // row within an 8-row group
   const int ec = (lane & 7) * 4;   // first of 4 columns
+  RowParts<Epi> rows;
+  if constexpr (col_row<Epi>()) rows.template init<FM>(epi, M, mw0, er);
 #pragma unroll
   for (int a = 0; a < FN; ++a) {
 #pragma unroll
@@ -596,10 +647,19 @@ GPT2_DEV void tile_epilogue(const f32x16_t (&acc)[FN][FM], const typename Epi::C
           v[i] = f32x4_t{t.x, t.y, t.z, t.w};
         }
         const int n = nw0 + a * 32 + ec;
+        if constexpr (col_row<Epi>()) {
+          const auto c = epi.col(n);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = mw0 + b * 32 + 8 * i + er;
-          if (m < M && n < N) epi.store(m, n, v[i], cx[a][b][i]);
+          for (int i = 0; i < 4; ++i) {
+            const int m = mw0 + b * 32 + 8 * i + er;
+            if (m < M && n < N) epi.store(rows.r[b * 4 + i], c, v[i], cx[a][b][i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = mw0 + b * 32 + 8 * i + er;
+            if (m < M && n < N) epi.store(m, n, v[i], cx[a][b][i]);
+          }
         }
       }
     }

@@ -11,8 +11,8 @@
 //    softmax in fp32 with exp2, MFMA 32x32x16 bf16 for Q K^T and P V.  Key tiles past the
 //    causal frontier are never loaded; tiles entirely above a wave's queries
 //    are skipped by that wave; only diagonal tiles apply the mask.
-//  * attn_rows_f32: one wave per query row with a full (max-subtracted)
-//    softmax, for the fp32 mode.
+//  * attn_rows: one wave per query row with a full (max-subtracted)
+//    softmax, for the fp32 mode and for bf16 head widths other than 64.
 //  * attn_decode_bf16: one new query per (sequence, head) streaming the cache
 //    with one 8-wave workgroup per (sequence, head); the waves' online
 //    softmax states merge in LDS.
@@ -289,19 +289,21 @@ void launch_attn_prefill_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int 
   attn_prefill_bf16_kernel<<<B * H * nqb, 256, 0, s>>>(q, kv, o, H, T, l_past, B * H, nqb, n_cu);
 }
 
-// ================================================================ row-wise (fp32)
+// ================================================================ row-wise (any head width)
 // One wave per query row: scores into LDS, row max, exp, sum, then lanes over
-// the head dimension accumulate p_j v_j and divide by the sum.
-__global__ __launch_bounds__(256) void attn_rows_f32_kernel(const float* __restrict__ q, KvView kv,
-                                                            float* __restrict__ o, int B, int H, int T,
-                                                            int dh, int l_past, int maxk) {
+// the head dimension accumulate p_j v_j and divide by the sum.  Arithmetic in
+// fp32; q, K, V and o in the mode's storage type (fp32, or bf16 for head
+// widths other than 64).
+template <typename Tio>
+__global__ __launch_bounds__(256) void attn_rows_kernel(const Tio* __restrict__ q, KvView kv, Tio* __restrict__ o,
+                                                        int B, int H, int T, int dh, int l_past, int maxk) {
   extern __shared__ float sbuf[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const long long row = (long long)blockIdx.x * 4 + wave;
   const bool active = row < (long long)B * H * T;
   float* s = sbuf + wave * maxk;
   int t = 0, b = 0, h = 0, nk = 0;
-  const float *qv = nullptr, *kb = nullptr, *vb = nullptr;
+  const Tio *qv = nullptr, *kb = nullptr, *vb = nullptr;
   float m = -INFINITY, l = 0.f;
   if (active) {
     t = (int)(row % T);
@@ -310,15 +312,15 @@ __global__ __launch_bounds__(256) void attn_rows_f32_kernel(const float* __restr
     h = bh - b * H;
     nk = l_past + t + 1;
     qv = q + row * dh;
-    kb = (const float*)kv.base + b * kv.sb + h * kv.sh;
+    kb = (const Tio*)kv.base + b * kv.sb + h * kv.sh;
     vb = kb + kv.skv;
     const float scale = 1.0f / sqrtf((float)dh);
     for (int j = lane; j < nk; j += 64) {
-      const float* kr = kb + (long long)j * dh;
+      const Tio* kr = kb + (long long)j * dh;
       float acc = 0.f;
       for (int c = 0; c < dh; c += 4) {
-        const float4 a = *reinterpret_cast<const float4*>(qv + c);
-        const float4 k4 = *reinterpret_cast<const float4*>(kr + c);
+        const float4 a = load4(qv + c);
+        const float4 k4 = load4(kr + c);
         acc = fmaf(a.x, k4.x, acc);
         acc = fmaf(a.y, k4.y, acc);
         acc = fmaf(a.z, k4.z, acc);
@@ -341,30 +343,38 @@ __global__ __launch_bounds__(256) void attn_rows_f32_kernel(const float* __restr
   __syncthreads();
   if (active) {
     const float inv = 1.0f / l;
-    float* orow = o + ((long long)b * T + t) * (H * dh) + h * dh;
+    Tio* orow = o + ((long long)b * T + t) * (H * dh) + h * dh;
     for (int c = lane; c < dh; c += 64) {
       float acc = 0.f;
-      for (int j = 0; j < nk; ++j) acc = fmaf(s[j], vb[(long long)j * dh + c], acc);
-      orow[c] = acc * inv;
+      for (int j = 0; j < nk; ++j) acc = fmaf(s[j], ActT<Tio>::load(vb + (long long)j * dh + c), acc);
+      ActT<Tio>::store(orow + c, acc * inv);
     }
   }
 }
 
-void launch_attn_rows_f32(const float* q, KvView kv, float* o, int B, int H, int T, int d_head,
-                          int l_past, hipStream_t s) {
+template <typename Tio>
+static void rows_launch(const Tio* q, KvView kv, Tio* o, int B, int H, int T, int d_head, int l_past,
+                        hipStream_t s) {
   const long long rows = (long long)B * H * T;
   const int maxk = l_past + T;
   const int blocks = (int)((rows + 3) / 4);
   // a row of scores per wave: 4 waves x maxk x 4 B, up to 128 KB at the
   // 8192-key limit the entry points enforce, beyond the 64 KB default
-  static const bool attr_set = [] {  // once, thread-safe
-    (void)hipFuncSetAttribute((const void*)attn_rows_f32_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+  static const bool attr_set = [] {  // once per type, thread-safe
+    (void)hipFuncSetAttribute((const void*)attn_rows_kernel<Tio>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               4 * 8192 * (int)sizeof(float));
     return true;
   }();
   (void)attr_set;
-  attn_rows_f32_kernel<<<blocks, 256, 4 * maxk * sizeof(float), s>>>(q, kv, o, B, H, T, d_head,
-                                                                     l_past, maxk);
+  attn_rows_kernel<Tio><<<blocks, 256, 4 * maxk * sizeof(float), s>>>(q, kv, o, B, H, T, d_head, l_past, maxk);
+}
+
+void launch_attn_rows(bool bf16, const void* q, KvView kv, void* o, int B, int H, int T, int d_head, int l_past,
+                      hipStream_t s) {
+  if (bf16)
+    rows_launch((const bf16_t*)q, kv, (bf16_t*)o, B, H, T, d_head, l_past, s);
+  else
+    rows_launch((const float*)q, kv, (float*)o, B, H, T, d_head, l_past, s);
 }
 
 // ================================================================ decode (bf16, d_h = 64)

@@ -33,7 +33,13 @@ using namespace gpt2;
 constexpr size_t kAlign = 256;
 constexpr size_t kHeader = 256;  // sticky device flags at offset 0
 constexpr long long kMaxTokens = 1LL << 24;
-constexpr int kMaxRowKeysF32 = 8192;  // fp32 row-wise attention keeps a row of scores in LDS
+constexpr int kMaxRowKeys = 8192;  // the row-wise attention keeps a row of scores in LDS
+
+// The MFMA attention kernels take bf16 with head width 64; fp32 and other
+// bf16 head widths run the row-wise kernel.
+bool rows_attention(const gpt2_hparams& hp, gpt2_mode mode) {
+  return mode == GPT2_FP32 || hp.n_embd / hp.n_head != 64;
+}
 
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -134,8 +140,7 @@ gpt2_status check_hparams(const gpt2_hparams* hp, gpt2_mode mode, bool need_mode
   const int d = hp->n_embd, h = hp->n_head;
   if (d <= 0 || h <= 0 || d % h != 0 || d > 2048 || d % 8 != 0) return GPT2_E_SHAPE;
   const int dh = d / h;
-  if (mode == GPT2_BF16 && dh != 64) return GPT2_E_SHAPE;
-  if (mode == GPT2_FP32 && (dh % 4 != 0 || dh > 128)) return GPT2_E_SHAPE;
+  if (dh % 4 != 0 || dh > 128) return GPT2_E_SHAPE;
   if (hp->n_ctx <= 0) return GPT2_E_SHAPE;
   if (!(hp->eps >= 0.f) || !std::isfinite(hp->eps)) return GPT2_E_SHAPE;
   if (need_model && (hp->n_vocab <= 0 || hp->n_layer <= 0)) return GPT2_E_SHAPE;
@@ -167,7 +172,7 @@ gpt2_status check_common(const gpt2_hparams& hp, gpt2_mode mode, int B, int T, i
                          size_t ws_bytes) {
   if (B < 1 || T < 1 || (long long)B * T > kMaxTokens) return GPT2_E_SHAPE;
   if (l_past < 0 || (long long)l_past + T > hp.n_ctx) return GPT2_E_POSITION;
-  if (mode == GPT2_FP32 && l_past + T > kMaxRowKeysF32) return GPT2_E_SHAPE;
+  if (rows_attention(hp, mode) && l_past + T > kMaxRowKeys) return GPT2_E_SHAPE;
   if (!ws) return GPT2_E_NULL;
   if (!ws_aligned(ws) || ws_bytes < layout(hp, mode, B, T).total) return GPT2_E_WORKSPACE;
   return GPT2_OK;
@@ -206,7 +211,7 @@ enum Kern {
 };
 const char* const kKernNames[K_COUNT] = {
     "embed", "layernorm", "gemm_c_attn", "gemm_attn_c_proj", "gemm_c_fc", "gemm_mlp_c_proj",
-    "gemm_lm_head", "attn_prefill", "attn_rows_f32", "attn_decode", "argmax", "loss"};
+    "gemm_lm_head", "attn_prefill", "attn_rows", "attn_decode", "argmax", "loss"};
 
 struct Timing {
   bool on = false;
@@ -299,8 +304,8 @@ struct Run {
 
     timed(K_GEMM_C_ATTN, s, [&] { launch_gemm(b16, a, w.attn_w, m, 3 * d, d, e, s); });
     // causal attention -> o [B, T, d]
-    if (!b16) {
-      timed(K_ATTN_ROWS, s, [&] { launch_attn_rows_f32((const float*)q, kv, (float*)o, B, H, T, dh, l_past, s); });
+    if (rows_attention(hp, mode)) {
+      timed(K_ATTN_ROWS, s, [&] { launch_attn_rows(b16, q, kv, o, B, H, T, dh, l_past, s); });
     } else if (decode) {
       timed(K_ATTN_DECODE, s, [&] { launch_attn_decode_bf16((const bf16_t*)q, kv, (bf16_t*)o, B, H, l_past, s); });
     } else {
@@ -474,7 +479,7 @@ gpt2_status decode_checks(const gpt2_hparams* hp, gpt2_mode mode, const gpt2_wei
   if (!al4(ids) || !al4(logits) || !al16(cache->data)) return GPT2_E_ALIGN;
   if (B < 1 || B > kMaxTokens) return GPT2_E_SHAPE;
   if (l_past < 0 || (long long)l_past + 1 > hp->n_ctx || l_past >= cache->capacity) return GPT2_E_POSITION;
-  if (mode == GPT2_FP32 && l_past + 1 > kMaxRowKeysF32) return GPT2_E_SHAPE;
+  if (rows_attention(*hp, mode) && l_past + 1 > kMaxRowKeys) return GPT2_E_SHAPE;
   return GPT2_OK;
 }
 
@@ -543,7 +548,7 @@ gpt2_status gpt2_generate_greedy(const gpt2_hparams* hp, gpt2_mode mode, const g
   if (B < 1 || n_new < 1 || B > kMaxTokens) return GPT2_E_SHAPE;
   if (l_past < 0 || (long long)l_past + n_new > hp->n_ctx || (long long)l_past + n_new > cache->capacity)
     return GPT2_E_POSITION;
-  if (mode == GPT2_FP32 && l_past + n_new > kMaxRowKeysF32) return GPT2_E_SHAPE;
+  if (rows_attention(*hp, mode) && l_past + n_new > kMaxRowKeys) return GPT2_E_SHAPE;
   const GenLayout G = gen_layout(*hp, mode, B);
   if (!ws_aligned(ws) || ws_bytes < G.total) return GPT2_E_WORKSPACE;
   (void)hipGetLastError();

@@ -91,9 +91,10 @@ void launch_loss_from_logits(const float* logits, const int32_t* targets, int M,
 // Prefill (bf16, d_h == 64, no past): flash kernel with MFMA.
 void launch_attn_prefill_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int T, int l_past,
                               hipStream_t s);
-// Row-wise reference-style kernel (fp32 mode, any T, d_h % 4 == 0, d_h <= 128).
-void launch_attn_rows_f32(const float* q, KvView kv, float* o, int B, int H, int T, int d_head,
-                          int l_past, hipStream_t s);
+// Row-wise kernel (any T up to 8192 keys, d_h % 4 == 0, d_h <= 128): the
+// fp32 mode, and bf16 head widths other than 64 (bf16 storage, fp32 math).
+void launch_attn_rows(bool bf16, const void* q, KvView kv, void* o, int B, int H, int T, int d_head, int l_past,
+                      hipStream_t s);
 // Single-token decode (bf16, d_h == 64): one workgroup per (sequence, head).
 void launch_attn_decode_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int l_past,
                              hipStream_t s);

@@ -67,7 +67,7 @@ def kind_of(name: str, prev_kind: str | None) -> str:
     if "attn_decode" in n:
         return "attn_decode"
     if "attn_rows" in n:
-        return "attn_rows_f32"
+        return "attn_rows"
     if "EpiQKV" in n:
         return "gemm_c_attn"
     if "EpiBiasGelu" in n:

@@ -71,10 +71,11 @@ typedef enum { GPT2_FP32 = 0, GPT2_BF16 = 1 } gpt2_mode;
 
 /* Model sizes ("Full Forward Pass", Overview: n_vocab, n_ctx, n_embd, n_head,
  * n_layer) and the LayerNorm epsilon (1e-5 on the pages).
- * Supported: n_embd % n_head == 0, n_embd <= 2048, n_embd % 8 == 0;
- * head width d_h = n_embd / n_head must be 64 in GPT2_BF16 mode and a multiple
- * of 4 no larger than 128 in GPT2_FP32 mode, where a call's l_past + T must
- * also stay within 8192 keys (else GPT2_E_SHAPE). */
+ * Supported: n_embd % n_head == 0, n_embd <= 2048, n_embd % 8 == 0; head
+ * width d_h = n_embd / n_head a multiple of 4 no larger than 128.  GPT2_BF16
+ * with d_h = 64 runs the MFMA attention kernels; GPT2_FP32, and GPT2_BF16
+ * with another d_h, run a row-wise attention kernel for which a call's
+ * l_past + T must stay within 8192 keys (else GPT2_E_SHAPE). */
 typedef struct {
   int32_t n_vocab, n_ctx, n_embd, n_head, n_layer;
   float eps;

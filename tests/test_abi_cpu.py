@@ -40,7 +40,9 @@ def test_workspace_size_host_logic():
     assert G.workspace_size(hp, G.FP32, 8, 1024) > big
     assert G.workspace_size(hp, 5, 1, 1) == 0
     assert G.workspace_size(G.hparams(n_embd=770, n_head=10), G.BF16, 1, 1) == 0  # d_h = 77
-    assert G.workspace_size(G.hparams(n_embd=64, n_head=4), G.BF16, 1, 1) == 0    # bf16 needs d_h 64
+    assert G.workspace_size(G.hparams(n_embd=64, n_head=4), G.BF16, 1, 1) > 0     # bf16 at d_h 16
+    assert G.workspace_size(G.hparams(n_embd=768, n_head=4), G.BF16, 1, 1) == 0   # d_h 192 > 128
+    assert G.workspace_size(G.hparams(n_embd=96, n_head=16), G.BF16, 1, 1) == 0   # d_h 6 not a multiple of 4
     assert G.workspace_size(G.hparams(n_embd=64, n_head=4), G.FP32, 1, 1) > 0
     assert G.workspace_size(hp, G.BF16, 0, 1) == 0
 

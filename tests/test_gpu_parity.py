@@ -103,6 +103,21 @@ def test_block_bf16_ragged(B, T, d):
     check("present", pres, opres, G.BF16)
 
 
+@pytest.mark.parametrize("affine", ["default", "random"])
+def test_block_d64_bf16(affine):
+    """The small block of the TorchCode page (d=64, 4 heads: head width 16)
+    in bf16: the row-wise attention kernel with bf16 storage."""
+    wl = WORKLOADS["block_d64_fp32"]
+    x = synth.hidden_input((wl.B, wl.T, wl.d), wl.seed, bf16=True)
+    w = synth.block_weights(wl.d, wl.seed, 0, affine=affine, bf16=True)
+    log(f"block bf16 d=64 h=4 x{x.shape} affine={affine}")
+    y, pres = run_block(G.BF16, wl.d, wl.h, x, w)
+    oy, opres = O.block_forward(x, w, wl.h)
+    assert y.shape == (2, 8, 64)
+    check("y", y, oy, G.BF16)
+    check("present", pres, opres, G.BF16)
+
+
 def test_block_gpt2s_bf16_full():
     """The single-block workload at full size (B=8, T=1024); sequences 0 and 7 vs the oracle."""
     wl = WORKLOADS["block_gpt2s_bf16"]
@@ -152,6 +167,9 @@ def _small_model(mode, V, n_ctx, d, h, L, seed):
     # the widest supported rows (n_embd 2048, 32 heads): LayerNorm at 8 groups
     # per lane, the register-staged product where the skinny one cannot take K
     (G.BF16, 301, 64, 2048, 32, 1, 1, 20),
+    # bf16 head widths other than 64 (16 and 128): the row-wise attention
+    (G.BF16, 1001, 256, 128, 8, 2, 2, 150),
+    (G.BF16, 1001, 128, 256, 2, 2, 1, 90),
 ])
 def test_forward_small(mode, V, n_ctx, d, h, L, B, T):
     W, Wd, hp = _small_model(mode, V, n_ctx, d, h, L, 400 + T)
@@ -280,6 +298,8 @@ def test_bad_token_sets_flag():
     (G.BF16, 211, 1024, 128, 2, 2, 3, 777),
     # B = 70 > 64: the decode step's products take the block kernels
     (G.BF16, 211, 128, 128, 2, 2, 70, 50),
+    # bf16 at head width 32: the row-wise attention in the decode step
+    (G.BF16, 211, 256, 128, 4, 2, 4, 130),
 ])
 def test_decode_matches_uncached(mode, V, n_ctx, d, h, L, B, T):
     """Forward over T-1 tokens into the cache, then one decode step of token T-1,

@@ -383,6 +383,10 @@ void launch_attn_rows(bool bf16, const void* q, KvView kv, void* o, int B, int H
 // wave, 8 lanes share a key row (8 dims each); a lane issues its RP K and RP V
 // row loads together (RP = 8: 16 KB in flight per wave, 100 VGPRs, so four
 // waves per SIMD and every workgroup of a 768-workgroup launch resident).
+// The cache rows are read once per step, with the non-temporal cache policy:
+// the 2.4 GB stream then leaves the weights, which every step re-reads, in
+// the last-level cache (decode step 0.825 -> 0.764 ms, attention 37.9 ->
+// 34.6 us per layer, head 23.0 -> 21.0 us).
 // Each wave keeps an online softmax (running max, partial sums per lane);
 // the waves then merge through LDS, so no second kernel is needed.
 constexpr int kDecWaves = 8, kDecRows = 8;  // measured best at 1024 keys, d_h 64
@@ -416,8 +420,8 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_bf16_kernel(const bf16_t*
 #pragma unroll
     for (int i = 0; i < RP; ++i) {
       const int key = min(k0 + rg + 8 * i, nk - 1);
-      kr[i] = *reinterpret_cast<const uint4*>(kbase + (long long)key * D + c8 * 8);
-      vr[i] = *reinterpret_cast<const uint4*>(vbase + (long long)key * D + c8 * 8);
+      kr[i] = load16_nt(kbase + (long long)key * D + c8 * 8);
+      vr[i] = load16_nt(vbase + (long long)key * D + c8 * 8);
     }
   };
   int key0 = wave * KP;

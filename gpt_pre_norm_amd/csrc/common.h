@@ -10,6 +10,7 @@ typedef uint16_t bf16_t;  // bfloat16 storage (bit pattern)
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 // f32x4 at 4-byte alignment (gfx9 vector memory accepts dword-aligned dwordx4)
 typedef __attribute__((__vector_size__(4 * sizeof(float)), __aligned__(4))) float f32x4u_t;
 
@@ -44,6 +45,13 @@ template <> struct ActT<bf16_t> {
   static GPT2_DEV float load(const bf16_t* p) { return bf2f(*p); }
   static GPT2_DEV void store(bf16_t* p, float v) { *p = f2bf(v); }
 };
+
+// 16 bytes read with the non-temporal (streaming) cache policy: for data
+// that is read once per call, so that it does not push data that later
+// kernels re-read out of the caches.
+GPT2_DEV uint4 load16_nt(const void* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
 
 // Four consecutive elements <-> float4 (16 B for fp32, 8 B for bf16).
 GPT2_DEV float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }

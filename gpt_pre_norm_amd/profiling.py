@@ -60,7 +60,8 @@ def kind_of(name: str, prev_kind: str | None) -> str:
     n = short_name(name)
     if "embed" in n:
         return "embed"
-    if "layernorm_kernel" in n:
+    if "layernorm_kernel" in n or "layernorm_reduce" in n:
+        # the reduce form also adds the residual product's partial sums
         return "layernorm"
     if "attn_prefill" in n:
         return "attn_prefill"
@@ -76,7 +77,7 @@ def kind_of(name: str, prev_kind: str | None) -> str:
         return "gemm_lm_head_loss"
     if "EpiStoreF32" in n:
         return "gemm_lm_head"
-    if "EpiResidInPlace" in n or "EpiBiasResid" in n:
+    if "EpiResidInPlace" in n or "EpiBiasResid" in n or "EpiPartial" in n:
         # the block's two residual products: after attention, after c_fc
         return "gemm_mlp_c_proj" if prev_kind == "gemm_c_fc" else "gemm_attn_c_proj"
     return n

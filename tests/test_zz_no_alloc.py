@@ -71,3 +71,38 @@ def test_noalloc_rejects_oversized_batch():
     with pytest.raises(G.Gpt2Error) as e:
         G.decode_step_noalloc(hp, G.BF16, Wd, ids, B, 3, cache, 16, logits)
     assert e.value.status == 5  # GPT2_E_WORKSPACE
+
+
+def test_noalloc_graph_replays_match_eager():
+    """The no-alloc step is meant for code under HIP graph capture: captured
+    once and replayed several times, with eager work between the replays,
+    every replay gives the eager no-alloc step's bits."""
+    V, n_ctx, d, h, L, B, T = 701, 128, 256, 4, 2, 16, 30
+    W = synth.model_weights(V, n_ctx, d, L, 1320, affine="random", bf16=True)
+    Wd, hp = G.upload_model(W, G.BF16), hp_of(V, n_ctx, d, h, L)
+    ids = synth.ids_input((B, T), V, 1321)
+    cache = new_cache(G.BF16, B, L, h, n_ctx, d // h)
+    _, st = run_forward(G.BF16, hp, Wd, ids[:, :T - 1], cache=cache, capacity=n_ctx)
+    assert st == 0
+    idd = torch.from_numpy(np.ascontiguousarray(ids[:, T - 1], np.int32)).cuda()
+    logits = torch.empty((B, 1, V), dtype=torch.float32, device="cuda")
+    G.decode_step_noalloc(hp, G.BF16, Wd, idd, B, T - 1, cache, n_ctx, logits)
+    torch.cuda.synchronize()
+    eager_logits, eager_kv = logits.clone(), cache[..., T - 1, :].clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        G.decode_step_noalloc(hp, G.BF16, Wd, idd, B, T - 1, cache, n_ctx, logits)
+    for rep in range(4):
+        logits.fill_(float("nan"))
+        cache[..., T - 1, :] = 0
+        graph.replay()
+        torch.cuda.synchronize()
+        same = torch.equal(logits, eager_logits) and torch.equal(cache[..., T - 1, :], eager_kv)
+        log(f"  no-alloc replay {rep}: identical to the eager step {same}")
+        assert same
+        # eager work between replays, on the same device array: a smaller
+        # no-alloc step of other sequences
+        c2 = new_cache(G.BF16, 3, L, h, n_ctx, d // h)
+        l2 = torch.empty((3, 1, V), dtype=torch.float32, device="cuda")
+        G.decode_step_noalloc(hp, G.BF16, Wd, idd[:3], 3, 5, c2, n_ctx, l2)
+        torch.cuda.synchronize()

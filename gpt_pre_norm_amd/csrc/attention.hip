@@ -279,13 +279,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16_t* __
 void launch_attn_prefill_bf16(const bf16_t* q, KvView kv, bf16_t* o, int B, int H, int T, int l_past,
                               hipStream_t s) {
   const int nqb = (T + 127) / 128;
-  static int n_cu = 0;
-  if (n_cu == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
-      n_cu = 256;
-  }
+  const int n_cu = device_cu_count();
   attn_prefill_bf16_kernel<<<B * H * nqb, 256, 0, s>>>(q, kv, o, H, T, l_past, B * H, nqb, n_cu);
 }
 
@@ -360,12 +354,7 @@ static void rows_launch(const Tio* q, KvView kv, Tio* o, int B, int H, int T, in
   const int blocks = (int)((rows + 3) / 4);
   // a row of scores per wave: 4 waves x maxk x 4 B, up to 128 KB at the
   // 8192-key limit the entry points enforce, beyond the 64 KB default
-  static const bool attr_set = [] {  // once per type, thread-safe
-    (void)hipFuncSetAttribute((const void*)attn_rows_kernel<Tio>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              4 * 8192 * (int)sizeof(float));
-    return true;
-  }();
-  (void)attr_set;
+  set_dynamic_lds_limit((const void*)attn_rows_kernel<Tio>, 4 * 8192 * (int)sizeof(float));
   attn_rows_kernel<Tio><<<blocks, 256, 4 * maxk * sizeof(float), s>>>(q, kv, o, B, H, T, d_head, l_past, maxk);
 }
 

@@ -820,14 +820,7 @@ template <int BM, int BN, int BK, int STAGES, class Epi, int WGM, int WGN>
 static void run_bf16_v3(const bf16_t* X, const bf16_t* W, int M, int N, int K, const Epi& epi,
                         hipStream_t s) {
   using C = V2Cfg<BM, BN, BK, STAGES, WGM * WGN>;
-  // once per template instance; a function-local static is initialised once
-  // even when several host threads launch concurrently
-  static const bool attr_set = [] {
-    (void)hipFuncSetAttribute((const void*)gemm_bf16_v3_kernel<BM, BN, BK, STAGES, WGM, WGN, Epi>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-    return true;
-  }();
-  (void)attr_set;
+  set_dynamic_lds_limit((const void*)gemm_bf16_v3_kernel<BM, BN, BK, STAGES, WGM, WGN, Epi>, (int)C::LDS_BYTES);
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN + (line_aligned<Epi>() ? 1 : 0);
   gemm_bf16_v3_kernel<BM, BN, BK, STAGES, WGM, WGN, Epi>
       <<<tiles_m * tiles_n, 64 * WGM * WGN, C::LDS_BYTES, s>>>(X, W, M, N, K, epi, tiles_m, tiles_n);
@@ -960,12 +953,7 @@ static void run_skinny(const bf16_t* X, const bf16_t* W, int M, int N, int K, in
   // the tile, and after the MFMAs the four waves' partial sums
   // (4 waves x NT/16 x 4 fragments x 64 lanes x 16 B = NT KB) in the same space
   const size_t lds = std::max((size_t)(64 + NT) * (K / S) * 2, (size_t)NT * 1024);
-  static const bool attr_set = [] {  // once per template instance, thread-safe
-    (void)hipFuncSetAttribute((const void*)gemm_skinny_kernel<NT, Epi>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    return true;
-  }();
-  (void)attr_set;
+  set_dynamic_lds_limit((const void*)gemm_skinny_kernel<NT, Epi>, 160 * 1024);
   const int nslices = (N + NT - 1) / NT;
   gemm_skinny_kernel<NT, Epi><<<nslices * S, 256, lds, s>>>(X, W, M, N, K, S, epi,
                                                              FastDiv::make((uint32_t)(K / S / 8)));
@@ -995,19 +983,8 @@ static bool try_skinny(const bf16_t* X, const bf16_t* W, int M, int N, int K, co
 // c_proj 164 -> 105 us, attn c_proj 50 -> 34 us).
 enum class Tiles { k128x192, k128x96, k128x256 };
 
-static int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
-}
-
 static Tiles block_tiles(int M, int N) {
-  const long long ncu = cu_count();
+  const long long ncu = device_cu_count();
   const long long tm = (M + 127) / 128;
   const long long t192 = tm * ((N + 191) / 192), t256 = tm * ((N + 255) / 256);
   if (2 * t192 <= ncu) return Tiles::k128x96;

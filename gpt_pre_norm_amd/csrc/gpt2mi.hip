@@ -15,7 +15,10 @@
 #include <cstddef>
 #include <algorithm>
 #include <cstdint>
+#include <atomic>
 #include <mutex>
+#include <set>
+#include <utility>
 #include <vector>
 
 #include "../../include/gpt2mi.h"
@@ -25,6 +28,39 @@
 // GPU the library runs on holds until the process ends (16 MiB).
 constexpr size_t kScratchBytes = 16u << 20;
 static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace gpt2 {
+
+namespace {
+constexpr int kMaxDeviceIds = 64;
+int current_device_id() {
+  int dev = 0;
+  return hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDeviceIds ? dev : -1;
+}
+}  // namespace
+
+int device_cu_count() {
+  static std::atomic<int> n[kMaxDeviceIds];
+  const int dev = current_device_id();
+  if (dev < 0) return 256;
+  int v = n[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    n[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+void set_dynamic_lds_limit(const void* fn, int bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<int, const void*>> done;
+  const int dev = current_device_id();
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 0 || done.emplace(dev, fn).second)
+    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+}  // namespace gpt2
 
 namespace {
 

@@ -10,6 +10,16 @@
 
 namespace gpt2 {
 
+// ---------------------------------------------------------------- per-device host facts
+// Device properties and function attributes belong to the device that is
+// current when they are read or set; both helpers act on the current device
+// and cache per device (thread-safe).
+// Compute units of the current device (256 if the query fails).
+int device_cu_count();
+// Raises fn's dynamic-LDS limit to `bytes` on the current device, once per
+// (device, kernel).
+void set_dynamic_lds_limit(const void* fn, int bytes);
+
 // ---------------------------------------------------------------- embedding
 // Embedding plus the first LayerNorm: x[m, :] (fp32) = wte[ids[m], :] +
 // wpe[l_past + m % T, :] and a = LN(x; g, b) in the act dtype, one pass per

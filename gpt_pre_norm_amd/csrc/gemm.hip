@@ -973,23 +973,58 @@ static bool try_skinny(const bf16_t* X, const bf16_t* W, int M, int N, int K, co
   return true;
 }
 
-// Tile shape for the block products (M > 64).  128x192 tiles, two
-// workgroups per CU, are the best shape while there are at least as many
-// tiles as CUs.  With fewer, half the CUs or more would idle: 128x96 tiles
-// (four waves) double the count (M = 4096, N = 768: mlp c_proj 42 -> 35 us,
-// attn c_proj 15 -> 12 us).  Between one and two tiles per CU the last round
-// runs partly empty: 128x256 tiles (one workgroup per CU, 32x128 per wave)
-// when they fit in one round (M = 4096, N = 1600: 288 -> 224 tiles, mlp
-// c_proj 164 -> 105 us, attn c_proj 50 -> 34 us).
-enum class Tiles { k128x192, k128x96, k128x256 };
+// Tile shape for the block products (M > 64), chosen by an estimate of the
+// busiest CU's time.  Each shape has a measured throughput per CU when its
+// workgroups fill the CU (fraction of the bf16 MFMA peak, random data,
+// M = 4096 and 8192 products of the GPT-2 depths); a CU left with one
+// workgroup of a two-per-CU shape in its last round runs at 0.8 of that.  The
+// estimate is the busiest CU's tile count in whole rounds of `per_cu`
+// workgroups, times the tile's area, over that throughput; K is common to
+// every shape.  On the 20 measured products it picks the fastest shape or one
+// within 6% of it (M = 4096, N = 1024: mlp c_proj 53.6 -> 47.1 us with
+// 128x128; N = 4096: c_fc 44.6 -> 40.3 us with 256x256), and keeps 128x192
+// for every GPT-2-small product at M = 8192.  128x256 and 256x192 tiles
+// measured no better than these anywhere.  256-row tiles are left out for the
+// residual epilogues, whose prefetched fp32 residual would not fit in
+// registers beside a 64-row wave tile.
+enum class Tiles { k128x192, k128x96, k128x128, k256x256 };
 
-static Tiles block_tiles(int M, int N) {
+struct TileShape {
+  Tiles id;
+  int bm, bn, per_cu;
+  double rate;
+};
+constexpr TileShape kTileShapes[] = {
+    {Tiles::k128x192, 128, 192, 2, 0.31},
+    {Tiles::k128x96, 128, 96, 2, 0.24},
+    {Tiles::k128x128, 128, 128, 2, 0.28},
+    {Tiles::k256x256, 256, 256, 1, 0.32},
+};
+
+static Tiles block_tiles(int M, int N, bool tall_ok) {
   const long long ncu = device_cu_count();
-  const long long tm = (M + 127) / 128;
-  const long long t192 = tm * ((N + 191) / 192), t256 = tm * ((N + 255) / 256);
-  if (2 * t192 <= ncu) return Tiles::k128x96;
-  if (t192 > ncu && t192 < 2 * ncu && t256 <= ncu) return Tiles::k128x256;
-  return Tiles::k128x192;
+  Tiles best = Tiles::k128x192;
+  double best_t = 0.0;
+  for (const TileShape& t : kTileShapes) {
+    if (t.bm == 256 && !tall_ok) continue;
+    const long long tiles = (long long)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+    const long long k = (tiles + ncu - 1) / ncu;  // tiles on the busiest CU
+    const long long rounds = k / t.per_cu, rem = k % t.per_cu;
+    const double area = (double)t.bm * t.bn;
+    double est = rounds * t.per_cu * area / t.rate;
+    if (rem) est += rem * area / (t.rate * (t.per_cu == 2 && rem == 1 ? 0.8 : 1.0));
+    if (best_t == 0.0 || est < best_t) {
+      best = t.id;
+      best_t = est;
+    }
+  }
+  return best;
+}
+
+// Epilogues that may take 256-row tiles: those without a prefetched residual.
+template <class Epi>
+constexpr bool tall_tiles_ok() {
+  return std::is_same_v<Epi, EpiBiasGelu<bf16_t>> || std::is_same_v<Epi, EpiQKV<bf16_t>>;
 }
 
 template <class Epi>
@@ -1017,9 +1052,13 @@ static void dispatch_bf16(const bf16_t* X, const bf16_t* W, int M, int N, int K,
       else
         run_bf16_v3<128, 192, 64, 2, EpiStoreF32Lines, 4, 2>(X, W, M, N, K, lines, s);
     } else {
-      switch (block_tiles(M, N)) {
+      constexpr bool tall_ok = tall_tiles_ok<Epi>();
+      switch (block_tiles(M, N, tall_ok)) {
         case Tiles::k128x96: run_bf16_v3<128, 96, 64, 2, Epi, 4, 1>(X, W, M, N, K, epi, s); break;
-        case Tiles::k128x256: run_bf16_v3<128, 256, 64, 2, Epi, 4, 2>(X, W, M, N, K, epi, s); break;
+        case Tiles::k128x128: run_bf16_v3<128, 128, 64, 2, Epi, 4, 2>(X, W, M, N, K, epi, s); break;
+        case Tiles::k256x256:
+          if constexpr (tall_ok) run_bf16_v3<256, 256, 64, 2, Epi, 4, 2>(X, W, M, N, K, epi, s);
+          break;
         default: run_bf16_v3<128, 192, 64, 2, Epi, 4, 2>(X, W, M, N, K, epi, s); break;
       }
     }

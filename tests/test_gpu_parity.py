@@ -91,7 +91,13 @@ def test_block_fp32_gelu_is_tanh_form():
     check("y", y, oy, G.FP32)
 
 
-@pytest.mark.parametrize("B,T,d", [(2, 200, 768), (3, 129, 128), (1, 1, 64), (2, 64, 192)])
+@pytest.mark.parametrize("B,T,d", [
+    (2, 200, 768), (3, 129, 128), (1, 1, 64), (2, 64, 192),
+    # 4000 rows, no multiple of 128 or 256: at d = 1024 the MLP's first
+    # product takes 256x256 tiles and the residual products 128x128; at
+    # d = 1280 the QKV product takes 256x256 and the MLP 128x128
+    (4, 1000, 1024), (4, 1000, 1280),
+])
 def test_block_bf16_ragged(B, T, d):
     h = d // 64
     x = synth.hidden_input((B, T, d), 200 + T, bf16=True)

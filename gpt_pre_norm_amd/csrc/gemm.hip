@@ -983,8 +983,9 @@ static bool try_skinny(const bf16_t* X, const bf16_t* W, int M, int N, int K, co
 // every shape.  On the 20 measured products it picks the fastest shape or one
 // within 6% of it (M = 4096, N = 1024: mlp c_proj 53.6 -> 47.1 us with
 // 128x128; N = 4096: c_fc 44.6 -> 40.3 us with 256x256), and keeps 128x192
-// for every GPT-2-small product at M = 8192.  128x256 and 256x192 tiles
-// measured no better than these anywhere.  256-row tiles are left out for the
+// for every GPT-2-small product at M = 8192.  128x256 and 256x192 tiles beat
+// these on a few products by 2-5% at most, within run-to-run variation, and
+// are left out.  256-row tiles are left out for the
 // residual epilogues, whose prefetched fp32 residual would not fit in
 // registers beside a 64-row wave tile.
 enum class Tiles { k128x192, k128x96, k128x128, k256x256 };
